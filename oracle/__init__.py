@@ -1,0 +1,32 @@
+"""Oracle for draft-tree verification: plain, slow, obviously correct CPU code.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call this
+package: only the tests, the smoke check and the benchmark's CPU-baseline leg
+use it. It shares no code with the HIP library (no kernels, headers, helpers or
+constant tables) and imports nothing from it.
+
+What it computes, and where the pages define it:
+
+* ``tree``       -- ancestor sets of a flattened prefix tree (DARTree paper,
+                    Preliminaries > Tree Verification and DDTree: each node sees
+                    the verified context and its root-to-node path).
+* ``attention``  -- tree attention in float64 with an explicit dense
+                    ancestor-only mask (same passage; DDTree abstract: one target
+                    forward with an ancestor-only attention mask).
+* ``argmax``     -- the target's greedy prediction per node, lowest index on
+                    ties (DARTree paper, Preliminaries > Speculative Sampling,
+                    the T = 0 rule).
+* ``walk``       -- the accepted root-to-leaf path and the bonus token (same
+                    passage, plus the bonus-token sentence of Speculative
+                    Sampling and the definition of tau in Experimental Setup).
+* ``build_tree`` -- the DDTree best-first heap (DARTree paper, Figure 3
+                    caption) and the top-mass optimum it reaches (Tree
+                    Verification and DDTree, eq. 4 and the mass decomposition
+                    after it; Lemma 1 with its proof in Appendix C).
+
+Parity pins: every function here is checked by tests/test_oracle_*.py against
+something other than itself (library routines, closed forms, brute force,
+hand-worked fixtures under tests/golden/). No function is left unpinned.
+"""
+
+from . import tree, attention, argmax, walk, build_tree  # noqa: F401
