@@ -1,0 +1,244 @@
+"""Draft-tree verification on MI355X: Python binding of libdtree.
+
+Same names as the C ABI (include/dtree.h). These wrappers only marshal
+arguments: numpy arrays for host data, torch CUDA tensors for device memory,
+the current torch stream as the HIP stream. Every step of the computation runs
+in libdtree (host C++ for the tree builder, HIP kernels for the rest).
+
+    dt_build_tree       best-first (DDTree) draft-tree construction, host
+    dt_tree_attention   ancestor-only tree attention over a KV-cached prefix
+    dt_argmax_rows      per-node greedy prediction (row arg-max, lowest index on ties)
+    dt_accept_path      longest accepted root-to-leaf path and bonus token
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import dt_attn_desc  # noqa: F401
+
+__all__ = [
+    "DtError", "dt_status_string", "dt_abi_version", "dt_build_tree", "dt_validate_tree",
+    "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention",
+    "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_accept_path", "library_path",
+]
+
+
+class DtError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {dt_status_string(status)} (status {status})")
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _check(status, where):
+    if status != _lib.DT_OK:
+        raise DtError(status, where)
+
+
+def dt_status_string(status):
+    return _lib.load().dt_status_string(int(status)).decode()
+
+
+def dt_abi_version():
+    return _lib.load().dt_abi_version()
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def dt_build_tree(cand_logprob, cand_token, root_token, n_nodes, with_score=True):
+    """Best-first tree over per-depth ranked candidates (host).
+
+    cand_logprob float32 [depths, k] (rows non-increasing, entries <= 0),
+    cand_token int32 [depths, k]. Returns (parent, token, depth, score) numpy
+    arrays of the realised node count (score is None if with_score=False).
+    """
+    lib = _lib.load()
+    lp = np.ascontiguousarray(cand_logprob, dtype=np.float32)
+    tok = _i32(cand_token)
+    if lp.ndim != 2 or lp.shape != tok.shape:
+        raise ValueError("cand_logprob and cand_token must be 2-D and of equal shape")
+    depths, k = lp.shape
+    n_nodes = int(n_nodes)
+    size = max(n_nodes, 1)
+    parent = np.empty(size, np.int32)
+    token = np.empty(size, np.int32)
+    depth = np.empty(size, np.int32)
+    score = np.empty(size, np.float64) if with_score else None
+    n_out = ctypes.c_int32(0)
+    st = lib.dt_build_tree(depths, k, _ptr(lp, ctypes.c_float), _ptr(tok, ctypes.c_int32), int(root_token), n_nodes,
+                           _ptr(parent, ctypes.c_int32), _ptr(token, ctypes.c_int32), _ptr(depth, ctypes.c_int32),
+                           _ptr(score, ctypes.c_double) if with_score else None, ctypes.byref(n_out))
+    _check(st, "dt_build_tree")
+    m = n_out.value
+    return parent[:m], token[:m], depth[:m], (score[:m] if with_score else None)
+
+
+def dt_validate_tree(parent):
+    """Status code (0 = valid) of a host parent array."""
+    p = _i32(parent)
+    return _lib.load().dt_validate_tree(_ptr(p, ctypes.c_int32) if p.size else None, int(p.size))
+
+
+class AttnLayout:
+    """Host-side sequence metadata of a (possibly ragged) batch of trees.
+
+    node_offsets int32 [S+1]; prefix_lens int32 [S]; prefix_row_start int64 [S]
+    (first cache row of each sequence; defaults to the packed layout).
+    """
+
+    def __init__(self, node_offsets, prefix_lens, prefix_row_start=None):
+        self.node_offsets = _i32(node_offsets)
+        self.prefix_lens = _i32(prefix_lens)
+        if prefix_row_start is None:
+            prefix_row_start = np.concatenate([[0], np.cumsum(self.prefix_lens, dtype=np.int64)[:-1]])
+        self.prefix_row_start = np.ascontiguousarray(prefix_row_start, dtype=np.int64)
+        if len(self.node_offsets) != len(self.prefix_lens) + 1 or len(self.prefix_row_start) != len(self.prefix_lens):
+            raise ValueError("node_offsets must have one more entry than prefix_lens / prefix_row_start")
+
+    @property
+    def num_seqs(self):
+        return len(self.prefix_lens)
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _desc(layout, Hq, Hkv, d, scale, split_keys, q_rs, out_rs, tree_rs, p_rs, p_hs):
+    desc = dt_attn_desc()
+    desc.num_seqs = layout.num_seqs
+    desc.num_q_heads = Hq
+    desc.num_kv_heads = Hkv
+    desc.head_dim = d
+    desc.softmax_scale = float(scale)
+    desc.split_keys = int(split_keys)
+    desc.node_offsets = _ptr(layout.node_offsets, ctypes.c_int32)
+    desc.prefix_lens = _ptr(layout.prefix_lens, ctypes.c_int32)
+    desc.prefix_row_start = _ptr(layout.prefix_row_start, ctypes.c_int64)
+    desc.q_row_stride = q_rs
+    desc.out_row_stride = out_rs
+    desc.tree_row_stride = tree_rs
+    desc.prefix_row_stride = p_rs
+    desc.prefix_head_stride = p_hs
+    return desc
+
+
+def _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys):
+    N, Hq, d = q.shape
+    Hkv = k_tree.shape[1]
+    for t, name in ((q, "q"), (k_tree, "k_tree")):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name}: heads must be contiguous [rows][heads][d]")
+    if k_prefix is not None and (k_prefix.stride(2) != 1):
+        raise ValueError("k_prefix: head_dim must be contiguous")
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    p_rs = k_prefix.stride(0) if k_prefix is not None else 0
+    p_hs = k_prefix.stride(1) if k_prefix is not None else 0
+    return _desc(layout, Hq, Hkv, d, scale, split_keys, q.stride(0), 0, k_tree.stride(0), p_rs, p_hs)
+
+
+def dt_tree_attention_workspace_size(q, k_tree, k_prefix, layout, scale=None, split_keys=0):
+    desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
+    n = ctypes.c_size_t(0)
+    _check(_lib.load().dt_tree_attention_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "dt_tree_attention_workspace_size")
+    return n.value
+
+
+def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, scale=None, split_keys=0,
+                      out=None, workspace=None, stream=None):
+    """Ancestor-only tree attention (GPU).
+
+    q [N, Hq, d], k_tree/v_tree [N, Hkv, d], k_prefix/v_prefix [rows, Hkv, d]
+    (any row/head strides, d contiguous; may be None when every prefix is
+    empty), parent int32 [N] tree-local, all torch CUDA tensors (bf16 for the
+    operands). Returns out [N, Hq, d] bf16.
+    """
+    import torch
+
+    if k_prefix is not None and (k_prefix.stride() != v_prefix.stride()):
+        raise ValueError("k_prefix and v_prefix must share strides")
+    if k_tree.stride() != v_tree.stride():
+        raise ValueError("k_tree and v_tree must share strides")
+    desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    desc.out_row_stride = out.stride(0)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _check(lib.dt_tree_attention_workspace_size(ctypes.byref(desc), ctypes.byref(need)),
+           "dt_tree_attention_workspace_size")
+    if need.value and workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.dt_tree_attention(ctypes.byref(desc), q.data_ptr(), k_tree.data_ptr(), v_tree.data_ptr(),
+                               k_prefix.data_ptr() if k_prefix is not None else None,
+                               v_prefix.data_ptr() if v_prefix is not None else None,
+                               parent.data_ptr(), out.data_ptr(), ws_ptr, ws_len, _stream(stream))
+    _check(st, "dt_tree_attention")
+    return out
+
+
+def dt_argmax_rows_workspace_size(rows, vocab):
+    n = ctypes.c_size_t(0)
+    _check(_lib.load().dt_argmax_rows_workspace_size(int(rows), int(vocab), ctypes.byref(n)),
+           "dt_argmax_rows_workspace_size")
+    return n.value
+
+
+def dt_argmax_rows(logits, out=None, workspace=None, stream=None):
+    """Per-row arg-max (lowest index on ties) of a [rows, vocab] float32 CUDA tensor
+    with unit column stride. Returns int32 [rows]."""
+    import torch
+
+    rows, vocab = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits: vocab dimension must be contiguous")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    need = dt_argmax_rows_workspace_size(rows, vocab)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dt_argmax_rows(logits.data_ptr(), rows, vocab, logits.stride(0), out.data_ptr(), ws_ptr, ws_len,
+                                    _stream(stream))
+    _check(st, "dt_argmax_rows")
+    return out
+
+
+def dt_accept_path(node_offsets, parent, token, argmax_idx, path=None, accept_len=None, bonus=None, stream=None):
+    """Longest accepted path per tree (GPU). node_offsets: host int32 [S+1];
+    parent/token/argmax_idx: int32 CUDA tensors [N]. Returns (path [N], accept_len [S], bonus [S])."""
+    import torch
+
+    offs = _i32(node_offsets)
+    S = len(offs) - 1
+    dev = parent.device
+    if path is None:
+        path = torch.empty(parent.shape[0], dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(S, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(S, dtype=torch.int32, device=dev)
+    st = _lib.load().dt_accept_path(S, _ptr(offs, ctypes.c_int32), parent.data_ptr(), token.data_ptr(),
+                                    argmax_idx.data_ptr(), path.data_ptr(), accept_len.data_ptr(), bonus.data_ptr(),
+                                    _stream(stream))
+    _check(st, "dt_accept_path")
+    return path, accept_len, bonus

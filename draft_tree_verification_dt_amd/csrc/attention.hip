@@ -1,0 +1,626 @@
+// Ancestor-only tree attention on gfx950.
+//
+// Operation (DARTree paper, Preliminaries > Tree Verification and DDTree; DDTree
+// abstract): every node of a flattened draft tree attends to the whole verified
+// prefix (already in the KV cache) and to the tree nodes on its own
+// root-to-node path, in one pass for all nodes.
+//
+// Design
+//  * Grouped-query packing: the g = Hq/Hkv query heads that share a KV head are
+//    packed with the tree's nodes into n*g query rows, so one KV head's keys
+//    meet a dense (n*g) x keys score block -- a real contraction for the
+//    matrix cores even though n is a few hundred at most.
+//  * A workgroup (4 waves) owns 128 query rows of one (sequence, KV head) and
+//    one chunk of that sequence's keys. Keys are visited in tiles of 64; each
+//    tile of K and V is staged in LDS once and read by all four waves. Two
+//    workgroups share a CU, so one's tile loads overlap the other's math.
+//  * Each wave holds 32 query rows. Scores are computed transposed,
+//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so that every lane ends up
+//    holding the scores of ONE query row: the softmax needs no cross-lane
+//    traffic except one exchange between the two half-waves, and the
+//    probabilities are already laid out as the B operand of O^T = V^T P^T.
+//    V is therefore staged transposed (V^T, d-major) in LDS.
+//  * Online softmax in the exp2 domain, fp32 statistics and accumulators;
+//    probabilities are rounded to bf16 (nearest-even) for the PV product.
+//  * Prefix keys need no mask. For tree keys the ancestor bitmask of each of
+//    the workgroup's nodes is built in LDS by walking parent pointers.
+//    Because parent[i] < i, a node's ancestors never exceed it, so tree keys
+//    beyond the workgroup's last node are skipped outright.
+//  * Sequences with too few row tiles to fill the GPU split their keys into
+//    chunks; partial (O, m, l) go to a workspace and a second kernel merges
+//    them with log-sum-exp weights.
+//  * Work items are remapped so that the row tiles sharing one KV chunk are
+//    dispatched to the same XCD (workgroups go round-robin over the 8 XCDs),
+//    which keeps that chunk's K/V in one L2.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+namespace dt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_bits;
+
+constexpr int kBM = 128;        // query rows per workgroup
+constexpr int kBN = 64;         // keys per tile
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kMaxSeqs = 32;    // sequences per launch (host loops over larger batches)
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct SeqGeom {
+  int64_t prefix_row0;  // first prefix row of this sequence
+  int32_t node_off;     // first node row
+  int32_t n;            // nodes
+  int32_t P;            // prefix length
+  int32_t splits;       // key chunks
+  int32_t row_tiles;    // ceil(n*g / kBM)
+  int32_t item_start;   // first work item
+  int32_t part_base;    // first partial row (split sequences), else -1
+  int32_t comb_start;   // first combine row (split sequences)
+};
+
+struct AttnParams {
+  const bf16_bits* q;
+  const bf16_bits* kt;
+  const bf16_bits* vt;
+  const bf16_bits* kp;
+  const bf16_bits* vp;
+  const int32_t* parent;
+  bf16_bits* out;
+  float* part_o;   // [part rows][D] unnormalised partial outputs
+  float2* part_ml; // [part rows] (running max in log2 units, sum)
+  int64_t q_rs, out_rs, t_rs, p_rs, p_hs;
+  float scale_log2;
+  int32_t Hq, Hkv, g;
+  int32_t chunk;        // keys per split
+  int32_t nseq;
+  int32_t total_items;
+  int32_t per_xcd;
+  int32_t mask_words;   // words per ancestor-mask row (>= ceil(max n / 32) + 2)
+  int32_t mask_rows;    // rows of the ancestor-mask table (max nodes per row tile)
+  int32_t max_n;
+  int32_t comb_rows;
+  SeqGeom seq[kMaxSeqs];
+};
+
+__device__ inline int find_seq(const AttnParams& p, int item) {
+  int s = 0;
+  for (int i = 1; i < p.nseq; ++i)
+    if (p.seq[i].item_start <= item) s = i;
+  return s;
+}
+
+// 16-byte (8 x bf16) global load.
+__device__ inline uint4 ld16(const bf16_bits* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
+
+// LDS layouts (D = head dim), padded so that every operand read is a per-lane
+// base address plus a compile-time offset and the MFMA operand reads are free
+// of bank conflicts:
+//  K tile   [64 keys][D + 8]   (row pitch / 16 bytes is odd)
+//  V^T tile [D][64 + 4 keys]   (consecutive d rows start 8 bytes apart in bank space)
+template <int D> struct Lds {
+  static constexpr int kPitch = D + 8;
+  static constexpr int vPitch = kBN + 4;
+  static constexpr int kElems = kBN * kPitch;
+  static constexpr int vElems = D * vPitch;
+};
+
+template <int D>
+struct TileLoader {
+  // Each thread moves 4 (D=128) or 2 (D=64) 16-byte chunks of K and of V per tile.
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kIters = kBN * kChunksPerRow / kThreads;
+  uint4 kreg[kIters];
+  uint4 vreg[kIters];
+
+  // Address of key `key` (sequence-local; prefix rows first, then tree nodes).
+  __device__ inline void load(const AttnParams& p, const SeqGeom& sg, int head, int kb, int key_end, int tid) {
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / kChunksPerRow;
+      const int c = idx % kChunksPerRow;
+      const int key = kb + r;
+      if (key < key_end) {
+        const bf16_bits *kptr, *vptr;
+        if (key < sg.P) {
+          const int64_t off = (sg.prefix_row0 + key) * p.p_rs + head * p.p_hs + c * 8;
+          kptr = p.kp + off;
+          vptr = p.vp + off;
+        } else {
+          const int64_t off = (int64_t)(sg.node_off + key - sg.P) * p.t_rs + head * D + c * 8;
+          kptr = p.kt + off;
+          vptr = p.vt + off;
+        }
+        kreg[it] = ld16(kptr);
+        vreg[it] = ld16(vptr);
+      } else {
+        kreg[it] = make_uint4(0, 0, 0, 0);
+        vreg[it] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ inline void store(bf16_bits* ks, bf16_bits* vts, int tid) {
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / kChunksPerRow;
+      const int c = idx % kChunksPerRow;
+      *reinterpret_cast<uint4*>(ks + r * Lds<D>::kPitch + c * 8) = kreg[it];
+      // V^T: the 8 values of key r, dims c*8 .. c*8+7, go to 8 different rows.
+      const bf16_bits* v = reinterpret_cast<const bf16_bits*>(&vreg[it]);
+      bf16_bits* dst = vts + (c * 8) * Lds<D>::vPitch + r;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j * Lds<D>::vPitch] = v[j];
+    }
+  }
+};
+
+// Bits [j0, j0 + cnt) of an ancestor-mask row, cnt <= 64, j0 >= 0.
+__device__ inline uint64_t mask_bits(const uint32_t* row, int j0, int cnt) {
+  const int w = j0 >> 5, off = j0 & 31;
+  uint64_t lo = (uint64_t)row[w] | ((uint64_t)row[w + 1] << 32);
+  uint64_t x = off ? ((lo >> off) | ((uint64_t)row[w + 2] << (64 - off))) : lo;
+  return cnt >= 64 ? x : (x & ((1ull << cnt) - 1));
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p) {
+  constexpr int KS = D / 16;  // k-steps of the QK^T product
+  constexpr int DB = D / 32;  // 32-wide blocks of the head dim
+  __shared__ __attribute__((aligned(16))) bf16_bits ks[Lds<D>::kElems];
+  __shared__ __attribute__((aligned(16))) bf16_bits vts[Lds<D>::vElems];
+  extern __shared__ uint32_t dyn[];  // [max_n] parents, then [mask_rows][mask_words] ancestor masks
+
+  // ---- work item (XCD-aware remap: consecutive items share an XCD) ----
+  const int b = blockIdx.x;
+  const int item = (b % kXcds) * p.per_xcd + b / kXcds;
+  if (item >= p.total_items) return;
+  const int s = find_seq(p, item);
+  const SeqGeom& sg = p.seq[s];
+  int local = item - sg.item_start;
+  const int tile = local % sg.row_tiles;
+  local /= sg.row_tiles;
+  const int split = local % sg.splits;
+  const int head = local / sg.splits;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;   // query row within the wave
+  const int hh = lane >> 5;   // half-wave
+  const int g = p.g;
+  const int nrows = sg.n * g;
+
+  const int row0 = tile * kBM;
+  const int my_row = row0 + wave * 32 + lr;
+  const bool row_ok = my_row < nrows;
+  const int my_node = row_ok ? my_row / g : 0;
+  const int my_qh = head * g + (row_ok ? my_row % g : 0);
+  const int node_lo = row0 / g;
+  const int node_hi = min(sg.n - 1, (min(row0 + kBM, nrows) - 1) / g);
+
+  // ---- key range of this work item ----
+  const int key_lo = split * p.chunk;
+  int key_hi = min(key_lo + p.chunk, sg.P + sg.n);
+  key_hi = min(key_hi, sg.P + node_hi + 1);  // later tree keys are no one's ancestor here
+  const int ntiles = key_hi > key_lo ? (key_hi - key_lo + kBN - 1) / kBN : 0;
+
+  uint32_t* par_s = dyn;
+  uint32_t* masks = dyn + p.max_n;
+
+  // ---- ancestor bitmasks of this tile's nodes (only if tree keys are visited) ----
+  if (key_hi > sg.P) {
+    for (int i = tid; i <= node_hi; i += kThreads) par_s[i] = (uint32_t)p.parent[sg.node_off + i];
+    const int nmask = (node_hi - node_lo + 1) * p.mask_words;
+    for (int i = tid; i < nmask; i += kThreads) masks[i] = 0u;
+    __syncthreads();
+    if (tid <= node_hi - node_lo) {
+      uint32_t* row = masks + tid * p.mask_words;
+      int j = node_lo + tid;
+      // Walk to the root; parent[j] < j bounds the walk even for a malformed array.
+      for (;;) {
+        row[j >> 5] |= 1u << (j & 31);
+        const int pj = (int)par_s[j];
+        if (pj < 0 || pj >= j) break;
+        j = pj;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- Q rows as the B operand of S^T = K Q^T: lane holds row lr, dims ks*16 + hh*8 .. +7 ----
+  bf16x8 qreg[KS];
+  {
+    const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint4 v = row_ok ? ld16(qrow + k * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+      qreg[k] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+  float m_run = -INFINITY;  // running max (log2 units), identical in both half-waves
+  float l_run = 0.f;        // running sum over this half-wave's keys
+
+  TileLoader<D> ld;
+  if (ntiles > 0) {
+    ld.load(p, sg, head, key_lo, key_hi, tid);
+    ld.store(ks, vts, tid);
+    __syncthreads();
+  }
+  const int prefix_end = min(sg.P, key_hi);  // keys below this are visible to every row
+  const uint32_t* my_mask = masks + (my_node - node_lo) * p.mask_words;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kb = key_lo + t * kBN;
+
+    // S^T block b (keys kb + 32b ..): lane (lr, hh) gets keys 32b + 8(i/4) + 4hh + (i%4), i = 0..15
+    f32x16 sc[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[bb][j] = 0.f;
+      const bf16_bits* kbase = ks + (bb * 32 + lr) * Lds<D>::kPitch + hh * 8;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + k * 16);
+        sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[k], sc[bb], 0, 0, 0);
+      }
+    }
+
+    // ---- scale, mask, online softmax ----
+    float tmax = -INFINITY;
+    if (kb + kBN <= prefix_end) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sc[bb][j] *= p.scale_log2;
+          tmax = fmaxf(tmax, sc[bb][j]);
+        }
+    } else {
+      // visibility of the 64 keys of this tile for my row
+      uint64_t vis = 0;
+      const int npre = prefix_end - kb;
+      if (npre > 0) vis = npre >= 64 ? ~0ull : ((1ull << npre) - 1);
+      const int tlo = max(sg.P, kb), thi = min(key_hi, kb + kBN);
+      if (row_ok && thi > tlo) vis |= mask_bits(my_mask, tlo - sg.P, thi - tlo) << (tlo - kb);
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kk = bb * 32 + (j >> 2) * 8 + hh * 4 + (j & 3);
+          const float v = ((vis >> kk) & 1ull) ? sc[bb][j] * p.scale_log2 : -INFINITY;
+          sc[bb][j] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = __builtin_amdgcn_exp2f(sc[bb][j] - m_use);
+        psum += e;
+        pb[bb][j >> 3][j & 7] = (__bf16)e;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+
+    // ---- O^T += V^T P^T: k-slots of half hh <-> keys 32bb + 16sub + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
+    const bf16_bits* vbase = vts + lr * Lds<D>::vPitch + hh * 4;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16_bits* vp = vbase + i * 32 * Lds<D>::vPitch + bb * 32 + sub * 16;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+          uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8*>(&a4), pb[bb][sub], acc[i], 0, 0, 0);
+        }
+    }
+
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      ld.load(p, sg, head, kb + kBN, key_hi, tid);
+      ld.store(ks, vts, tid);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane (lr, hh) holds O^T[d][row lr] for d = 32i + 8(j/4) + 4hh + (j%4) ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  if (sg.splits == 1) {
+    const float inv = 1.f / l_tot;
+    bf16_bits* orow = p.out + (int64_t)(sg.node_off + my_node) * p.out_rs + (int64_t)my_qh * D;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        __bf16 o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[i][j4 * 4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + i * 32 + j4 * 8 + hh * 4) = *reinterpret_cast<uint2*>(o4);
+      }
+  } else {
+    const int64_t prow = (int64_t)sg.part_base + ((int64_t)split * sg.n + my_node) * p.Hq + my_qh;
+    float* po = p.part_o + prow * D;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        *reinterpret_cast<float4*>(po + i * 32 + j4 * 8 + hh * 4) =
+            make_float4(acc[i][j4 * 4], acc[i][j4 * 4 + 1], acc[i][j4 * 4 + 2], acc[i][j4 * 4 + 3]);
+    if (hh == 0) p.part_ml[prow] = make_float2(m_run, l_tot);
+  }
+}
+
+// Merge the per-chunk partials of split sequences: one wave per (node, query head).
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.comb_rows) return;
+  int s = -1;
+  for (int i = 0; i < p.nseq; ++i)
+    if (p.seq[i].splits > 1 && p.seq[i].comb_start <= row) s = i;
+  if (s < 0) return;
+  const SeqGeom& sg = p.seq[s];
+  const int r = row - sg.comb_start;  // = node * Hq + qh
+  if (r >= sg.n * p.Hq) return;
+  const int node = r / p.Hq, qh = r % p.Hq;
+  float m = -INFINITY;
+  for (int k = 0; k < sg.splits; ++k) {
+    const int64_t prow = (int64_t)sg.part_base + ((int64_t)k * sg.n + node) * p.Hq + qh;
+    m = fmaxf(m, p.part_ml[prow].x);
+  }
+  constexpr int E = D / 64;  // elements per lane
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float l = 0.f;
+  for (int k = 0; k < sg.splits; ++k) {
+    const int64_t prow = (int64_t)sg.part_base + ((int64_t)k * sg.n + node) * p.Hq + qh;
+    const float2 ml = p.part_ml[prow];
+    if (ml.x == -INFINITY) continue;  // chunk saw no visible key for this row
+    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    l += w * ml.y;
+    const float* po = p.part_o + prow * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += w * po[e];
+  }
+  const float inv = 1.f / l;
+  bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    __bf16 v = (__bf16)(o[e] * inv);
+    orow[e] = *reinterpret_cast<bf16_bits*>(&v);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct Plan {
+  std::vector<AttnParams> launches;  // one per group of <= kMaxSeqs sequences
+  std::vector<int> grid;             // workgroups per launch
+  std::vector<int> comb_grid;        // combine blocks per launch (0 = none)
+  std::vector<size_t> lds;           // dynamic LDS bytes per launch
+  size_t ws_bytes = 0;
+};
+
+int check_desc(const dt_attn_desc* d) {
+  if (!d) return DT_ERR_NULL;
+  if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return DT_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads) return DT_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return DT_ERR_UNSUPPORTED;
+  if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale)) return DT_ERR_SHAPE;
+  if (d->split_keys < 0 || d->split_keys % kBN) return DT_ERR_SHAPE;
+  if (!d->node_offsets || !d->prefix_lens || !d->prefix_row_start) return DT_ERR_NULL;
+  if (d->node_offsets[0] != 0) return DT_ERR_SHAPE;
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int n = d->node_offsets[s + 1] - d->node_offsets[s];
+    if (n < 1 || n > DT_MAX_TREE_NODES) return n < 1 ? DT_ERR_SHAPE : DT_ERR_UNSUPPORTED;
+    if (d->prefix_lens[s] < 0 || d->prefix_row_start[s] < 0) return DT_ERR_SHAPE;
+  }
+  const int64_t D = d->head_dim;
+  const int64_t qrs = d->q_row_stride ? d->q_row_stride : d->num_q_heads * D;
+  const int64_t ors = d->out_row_stride ? d->out_row_stride : d->num_q_heads * D;
+  const int64_t trs = d->tree_row_stride ? d->tree_row_stride : d->num_kv_heads * D;
+  if (qrs < d->num_q_heads * D || ors < d->num_q_heads * D || trs < d->num_kv_heads * D) return DT_ERR_SHAPE;
+  if (qrs % 8 || ors % 8 || trs % 8 || d->prefix_row_stride % 8 || d->prefix_head_stride % 8) return DT_ERR_SHAPE;
+  if (d->prefix_row_stride < 0 || d->prefix_head_stride < 0) return DT_ERR_SHAPE;
+  return DT_OK;
+}
+
+int make_plan(const dt_attn_desc* d, Plan* plan) {
+  int st = check_desc(d);
+  if (st != DT_OK) return st;
+  int cus = 0;
+  st = current_device_cus(&cus);
+  if (st != DT_OK) return st;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  const int D = d->head_dim;
+
+  // Keys per split: automatic sizing aims for about 4 workgroups per CU in total.
+  int64_t chunk = d->split_keys;
+  if (chunk == 0) {
+    int64_t base_wg = 0, max_keys = 0, total_tiles = 0;
+    for (int s = 0; s < d->num_seqs; ++s) {
+      const int n = d->node_offsets[s + 1] - d->node_offsets[s];
+      const int64_t rt = ceil_div((int64_t)n * g, kBM) * d->num_kv_heads;
+      base_wg += rt;
+      const int64_t keys = (int64_t)d->prefix_lens[s] + n;
+      max_keys = std::max(max_keys, keys);
+      total_tiles += rt * ceil_div(keys, kBN);
+    }
+    const int64_t target = 4LL * cus;
+    if (base_wg >= target) {
+      chunk = ceil_div(max_keys, kBN) * kBN;  // no split
+    } else {
+      // tiles per workgroup so that the total is ~target, at least 8 tiles (512 keys)
+      int64_t tiles = std::max<int64_t>(8, ceil_div(total_tiles, target));
+      chunk = tiles * kBN;
+    }
+  }
+  if (chunk > (int64_t)1 << 30) chunk = (int64_t)1 << 30;
+
+  size_t part_rows = 0;
+  for (int s0 = 0; s0 < d->num_seqs; s0 += kMaxSeqs) {
+    AttnParams a;
+    std::memset(&a, 0, sizeof(a));
+    a.nseq = std::min(kMaxSeqs, d->num_seqs - s0);
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.g = g;
+    a.chunk = (int32_t)chunk;
+    a.scale_log2 = d->softmax_scale * kLog2e;
+    int items = 0, comb = 0, max_n = 1;
+    for (int i = 0; i < a.nseq; ++i) {
+      const int s = s0 + i;
+      SeqGeom& sg = a.seq[i];
+      sg.node_off = d->node_offsets[s];
+      sg.n = d->node_offsets[s + 1] - d->node_offsets[s];
+      sg.P = d->prefix_lens[s];
+      sg.prefix_row0 = d->prefix_row_start[s];
+      sg.row_tiles = (int32_t)ceil_div((int64_t)sg.n * g, kBM);
+      sg.splits = (int32_t)std::max<int64_t>(1, ceil_div((int64_t)sg.P + sg.n, chunk));
+      sg.item_start = items;
+      items += sg.row_tiles * sg.splits * d->num_kv_heads;
+      if (sg.splits > 1) {
+        sg.part_base = (int32_t)part_rows;
+        part_rows += (size_t)sg.splits * sg.n * d->num_q_heads;
+        sg.comb_start = comb;
+        comb += sg.n * d->num_q_heads;
+      } else {
+        sg.part_base = -1;
+        sg.comb_start = -1;
+      }
+      max_n = std::max(max_n, sg.n);
+    }
+    if (part_rows > (size_t)INT32_MAX) return DT_ERR_UNSUPPORTED;
+    a.total_items = items;
+    a.per_xcd = (int32_t)ceil_div(items, kXcds);
+    a.max_n = max_n;
+    a.mask_words = (max_n + 31) / 32 + 2;
+    a.mask_rows = (kBM - 1) / g + 2;
+    a.comb_rows = comb;
+    plan->launches.push_back(a);
+    plan->grid.push_back(a.per_xcd * kXcds);
+    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 4) : 0);
+    plan->lds.push_back(sizeof(uint32_t) * ((size_t)a.max_n + (size_t)a.mask_rows * a.mask_words));
+  }
+  (void)D;
+  plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(float), 256) +
+                                   round_up(part_rows * sizeof(float2), 256)
+                             : 0;
+  return DT_OK;
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_tree_attention_workspace_size(const dt_attn_desc* desc, size_t* bytes) {
+  if (!bytes) return DT_ERR_NULL;
+  dt::Plan plan;
+  int st = dt::make_plan(desc, &plan);
+  if (st != DT_OK) return st;
+  *bytes = plan.ws_bytes;
+  return DT_OK;
+}
+
+extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
+                                 const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dt;
+  if (!q || !k_tree || !v_tree || !parent || !out) return DT_ERR_NULL;
+  Plan plan;
+  int st = make_plan(desc, &plan);
+  if (st != DT_OK) return st;
+  bool any_prefix = false;
+  for (int s = 0; s < desc->num_seqs; ++s) any_prefix |= desc->prefix_lens[s] > 0;
+  if (any_prefix && (!k_prefix || !v_prefix)) return DT_ERR_NULL;
+  for (const void* ptr : {q, k_tree, v_tree, (const void*)out})
+    if (!aligned(ptr, 16)) return DT_ERR_SHAPE;
+  if (any_prefix && (!aligned(k_prefix, 16) || !aligned(v_prefix, 16))) return DT_ERR_SHAPE;
+  if (!aligned(parent, 4)) return DT_ERR_SHAPE;
+  if (plan.ws_bytes) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return DT_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DT_ERR_WORKSPACE;
+  }
+
+  const int64_t D = desc->head_dim;
+  const int64_t qrs = desc->q_row_stride ? desc->q_row_stride : desc->num_q_heads * D;
+  const int64_t ors = desc->out_row_stride ? desc->out_row_stride : desc->num_q_heads * D;
+  const int64_t trs = desc->tree_row_stride ? desc->tree_row_stride : desc->num_kv_heads * D;
+  size_t part_rows_bytes = 0;
+  for (auto& a : plan.launches)
+    for (int i = 0; i < a.nseq; ++i)
+      if (a.seq[i].splits > 1)
+        part_rows_bytes = std::max(part_rows_bytes,
+                                   (size_t)(a.seq[i].part_base + (size_t)a.seq[i].splits * a.seq[i].n * a.Hq));
+  float* part_o = static_cast<float*>(workspace);
+  float2* part_ml = plan.ws_bytes
+                        ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                                    round_up(part_rows_bytes * D * sizeof(float), 256))
+                        : nullptr;
+
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  for (size_t li = 0; li < plan.launches.size(); ++li) {
+    AttnParams a = plan.launches[li];
+    a.q = static_cast<const bf16_bits*>(q);
+    a.kt = static_cast<const bf16_bits*>(k_tree);
+    a.vt = static_cast<const bf16_bits*>(v_tree);
+    a.kp = static_cast<const bf16_bits*>(k_prefix);
+    a.vp = static_cast<const bf16_bits*>(v_prefix);
+    a.parent = parent;
+    a.out = static_cast<bf16_bits*>(out);
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.q_rs = qrs;
+    a.out_rs = ors;
+    a.t_rs = trs;
+    a.p_rs = desc->prefix_row_stride;
+    a.p_hs = desc->prefix_head_stride;
+    if (a.total_items == 0) continue;
+    if (D == 128) {
+      hipLaunchKernelGGL(tree_attn_fwd<128>, dim3(plan.grid[li]), dim3(kThreads), plan.lds[li], st_, a);
+      if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<128>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+    } else {
+      hipLaunchKernelGGL(tree_attn_fwd<64>, dim3(plan.grid[li]), dim3(kThreads), plan.lds[li], st_, a);
+      if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<64>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+    }
+    st = launch_status();
+    if (st != DT_OK) return st;
+  }
+  return DT_OK;
+}

@@ -1,0 +1,249 @@
+/*
+ * dtree.h -- C ABI of libdtree: verifying a draft tree in one target forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Speculative decoding with draft trees (DARTree: "Speculative Diffusion
+ * Decoding with Autoregressive Draft Trees", Preliminaries > Tree Verification
+ * and DDTree; DDTree: "Accelerating Speculative Decoding with Block Diffusion
+ * Draft Trees", abstract) verifies a whole prefix tree of draft tokens in a
+ * single target forward: the tree's nodes are flattened, each node attends to
+ * the verified context plus the nodes on its own root-to-node path (an
+ * ancestor-only mask), the target's greedy prediction is taken at every node,
+ * and the longest root-to-leaf path whose tokens match those predictions is
+ * accepted, followed by one bonus token.
+ *
+ * This library provides that path:
+ *   dt_build_tree       host: best-first (DDTree) tree construction
+ *   dt_tree_attention   GPU:  ancestor-only tree attention over a KV-cached prefix
+ *   dt_argmax_rows      GPU:  per-node greedy prediction (row arg-max)
+ *   dt_accept_path      GPU:  longest accepted path and bonus token
+ *
+ * Conventions shared by every entry point
+ *  - Every function returns an int status: DT_OK (0) or a negative DT_ERR_*.
+ *    Nothing throws across this boundary, aborts or prints.
+ *  - Ownership: the caller owns every buffer, host and device. The library
+ *    allocates no device memory (scratch comes from a caller-provided
+ *    workspace), uses host memory only for temporaries freed before the call
+ *    returns, and keeps no pointer after a call returns.
+ *  - Device work is enqueued on the caller's HIP stream, passed as `void*`
+ *    (a hipStream_t; NULL means the default stream). Outputs are valid once
+ *    the stream reaches that point. No call synchronises the stream.
+ *  - Arguments are validated before anything is enqueued; an invalid call
+ *    leaves every output untouched. Device data that cannot be read on the
+ *    host (device parent/token arrays, logits) is the caller's contract, as
+ *    stated per call; a violated device-side contract gives unspecified
+ *    results but never an out-of-bounds access.
+ *  - DT_ERR_HIP reports a failed HIP runtime call (e.g. a launch error); an
+ *    asynchronous device fault surfaces at the caller's next synchronisation.
+ *  - The library keeps no mutable global state (device properties are cached
+ *    once per device), so calls from several host threads are safe.
+ *
+ * Tree representation (all calls): a tree of n nodes is an int32 array
+ * parent[n] with parent[0] == -1 (node 0 is the root: the last committed
+ * token, whose logits predict draft position 1) and 0 <= parent[i] < i for
+ * i > 0, i.e. nodes are numbered in a topological order. Several trees are
+ * packed back to back; node_offsets[s] .. node_offsets[s+1]-1 are the rows
+ * of tree s and its parent entries are local to the tree.
+ */
+#ifndef DTREE_H
+#define DTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dt_status {
+  DT_OK = 0,
+  DT_ERR_NULL = -1,        /* a required pointer is NULL */
+  DT_ERR_SHAPE = -2,       /* a count, size, stride or offset is out of range or misaligned */
+  DT_ERR_TREE = -3,        /* a (host) parent array is not a topologically numbered tree */
+  DT_ERR_VALUE = -4,       /* candidate table: unsorted row, non-finite or positive log-prob, repeated token */
+  DT_ERR_UNSUPPORTED = -5, /* a valid request this build does not implement (e.g. head_dim not 64/128) */
+  DT_ERR_WORKSPACE = -6,   /* workspace NULL, too small or not 256-byte aligned */
+  DT_ERR_HIP = -7,         /* a HIP runtime call failed */
+  DT_ERR_NOMEM = -8        /* temporary host memory could not be obtained (dt_build_tree) */
+};
+
+/* Largest tree (nodes per sequence, root included) dt_tree_attention accepts. */
+#define DT_MAX_TREE_NODES 1024
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* dt_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int dt_abi_version(void);
+
+/*
+ * dt_build_tree -- DDTree best-first construction of a draft tree (host).
+ *
+ * Defined by: DARTree paper, Figure 3 caption (a max-heap over frontier
+ * prefixes: each pop takes the prefix of highest mass, which becomes a node,
+ * and pushes its next sibling and its first, highest-probability child); the
+ * objective it maximises is eq. 4 with the mass decomposition that follows it
+ * (Tree Verification and DDTree): the sum over tree prefixes of the product
+ * of their per-position draft probabilities. Lemma 1 (Deferred Best-First
+ * Pruning, eq. 6) shows the result equals global top-B selection when every
+ * step adds a non-positive log-probability and ancestors win ties.
+ *
+ * Inputs (host):
+ *   depths       number of draft positions (the drafting block, e.g. 16); 1..64
+ *   k            candidates per position; 1..65535
+ *   cand_logprob [depths][k] row-major float: log-probability of the r-th
+ *                candidate at each position. Every entry finite and <= 0;
+ *                each row non-increasing (ties in any token order).
+ *   cand_token   [depths][k] row-major int32 token ids, >= 0, distinct within a row.
+ *   root_token   token of the root (the last committed token), >= 0.
+ *   n_nodes      node budget counting the root (>= 1): the tree gets the root
+ *                plus up to n_nodes - 1 draft prefixes.
+ * Outputs (host, caller-allocated, n_nodes entries each; entries past n_out
+ * are left untouched):
+ *   parent       parent[0] = -1; parent[i] < i (pop order is topological)
+ *   token        token[0] = root_token; token[i] = the candidate's token id
+ *   depth        depth[0] = 0; depth[i] = draft position of node i (1-based)
+ *   score        nullable; log-mass of each node (sum of its candidates'
+ *                log-probs added root-first in double; score[0] = 0)
+ *   n_out        number of nodes written: n_nodes, or fewer if the table has
+ *                fewer prefixes.
+ * Order: nodes are emitted in pop order, i.e. by (score descending, depth
+ * ascending, rank tuple ascending lexicographically), which every parent
+ * precedes its children in.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE (sizes), DT_ERR_VALUE (table contract).
+ */
+int dt_build_tree(int32_t depths, int32_t k, const float* cand_logprob, const int32_t* cand_token,
+                  int32_t root_token, int32_t n_nodes, int32_t* parent, int32_t* token, int32_t* depth,
+                  double* score, int32_t* n_out);
+
+/*
+ * dt_validate_tree -- check a host parent array against the tree
+ * representation above. Returns DT_OK, DT_ERR_NULL (parent NULL with n > 0),
+ * DT_ERR_SHAPE (n < 1) or DT_ERR_TREE.
+ */
+int dt_validate_tree(const int32_t* parent, int32_t n);
+
+/*
+ * Description of one tree-attention call. Counts and strides in elements.
+ *
+ * Sequences: S trees, tree s has n_s = node_offsets[s+1] - node_offsets[s]
+ * nodes (1..DT_MAX_TREE_NODES) and a verified prefix of P_s = prefix_lens[s]
+ * tokens (>= 0) already in the KV cache at rows
+ * prefix_row_start[s] .. prefix_row_start[s] + P_s - 1 of k_prefix/v_prefix.
+ * The host arrays are read during the call only (they fix the launch
+ * geometry and are passed to the kernels by value).
+ */
+typedef struct dt_attn_desc {
+  int32_t num_seqs;              /* S >= 1 */
+  int32_t num_q_heads;           /* Hq >= 1 */
+  int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;              /* d: 64 or 128 */
+  float softmax_scale;           /* > 0 and finite; conventionally 1 / sqrt(d) */
+  int32_t split_keys;            /* 0: automatic. > 0: process each sequence's keys in chunks of
+                                    this many keys (a multiple of 64) and merge; for testing/tuning */
+  const int32_t* node_offsets;   /* host [S+1]; node_offsets[0] = 0, increasing */
+  const int32_t* prefix_lens;    /* host [S] */
+  const int64_t* prefix_row_start; /* host [S] */
+  int64_t q_row_stride;          /* elements between consecutive nodes in q; 0 means Hq*d */
+  int64_t out_row_stride;        /* ... in out; 0 means Hq*d */
+  int64_t tree_row_stride;       /* ... in k_tree and v_tree; 0 means Hkv*d */
+  int64_t prefix_row_stride;     /* elements between consecutive cache rows of k_prefix/v_prefix */
+  int64_t prefix_head_stride;    /* elements between consecutive KV heads within a cache row */
+} dt_attn_desc;
+
+/*
+ * dt_tree_attention_workspace_size -- bytes of device workspace that
+ * dt_tree_attention needs for this description on the current device (0 when
+ * no sequence is split). Errors as dt_tree_attention's host checks.
+ */
+int dt_tree_attention_workspace_size(const dt_attn_desc* desc, size_t* bytes);
+
+/*
+ * dt_tree_attention -- ancestor-only tree attention (GPU).
+ *
+ * Defined by: DARTree paper, Preliminaries > Tree Verification and DDTree
+ * (flattened nodes; each node attends only to the verified context and the
+ * tokens on its root-to-node path, so one target forward scores every
+ * branch); DDTree abstract (ancestor-only attention mask). For tree s, node i
+ * and query head h, with g = Hq / Hkv and kv = h / g:
+ *   keys    = prefix rows 0..P_s-1, then tree nodes j of tree s with j on the
+ *             path root..i (i included); every other tree node is invisible
+ *   out[i,h] = sum_j softmax_j(scale * <q[i,h], k_j>) * v_j
+ * The mask is derived in-kernel from `parent`; no dense mask is formed.
+ * Q and K are expected post-rotary (the caller places node i at position
+ * P_s + depth(i)).
+ *
+ * Device buffers (bf16 = IEEE bfloat16, 16-byte aligned; strides multiples of 8):
+ *   q        [N][Hq][d] with row stride q_row_stride; N = node_offsets[S]
+ *   k_tree   [N][Hkv][d], v_tree likewise, row stride tree_row_stride
+ *   k_prefix row r, head h at k_prefix + r*prefix_row_stride + h*prefix_head_stride
+ *            (d contiguous elements); v_prefix likewise with the same strides
+ *   parent   int32 [N], tree-local parents (contract: the tree representation
+ *            above; violating it gives unspecified values, never a fault)
+ *   out      [N][Hq][d] bf16, row stride out_row_stride; must not alias inputs
+ *   workspace  device scratch of at least dt_tree_attention_workspace_size
+ *            bytes, 256-byte aligned (may be NULL when that size is 0). The
+ *            library neither needs it zeroed nor preserves its contents.
+ * Arithmetic: bf16 operands, fp32 scores/softmax/accumulation, probabilities
+ * rounded to bf16 (nearest-even) for the value product, output rounded to bf16.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_UNSUPPORTED, DT_ERR_WORKSPACE, DT_ERR_HIP.
+ */
+int dt_tree_attention(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
+                      const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dt_argmax_rows_workspace_size -- bytes of device workspace dt_argmax_rows
+ * needs for `rows` rows of `vocab` entries on the current device.
+ */
+int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes);
+
+/*
+ * dt_argmax_rows -- the target's greedy prediction at every node (GPU).
+ *
+ * Defined by: DARTree paper, Preliminaries > Speculative Sampling: at T = 0
+ * a draft token is accepted when it equals the target model's greedy
+ * prediction. out_idx[r] = the lowest j in [0, vocab) with
+ * logits[r*row_stride + j] == max over the row (IEEE compare: -0 == +0).
+ *   logits     device float32, rows x vocab, row stride row_stride >= vocab;
+ *              4-byte aligned. Contract: finite values (a NaN gives an
+ *              unspecified index in [0, vocab)).
+ *   rows >= 0 (0 is a no-op), 1 <= vocab < 2^31
+ *   out_idx    device int32 [rows]
+ *   workspace  device scratch, >= dt_argmax_rows_workspace_size bytes,
+ *              256-byte aligned; may be NULL when that size is 0.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_WORKSPACE, DT_ERR_HIP.
+ */
+int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t* out_idx,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dt_accept_path -- longest accepted root-to-leaf path and bonus token (GPU).
+ *
+ * Defined by: DARTree paper, Preliminaries > Speculative Sampling (T = 0:
+ * accept consecutive draft tokens equal to the target's greedy predictions;
+ * at the first mismatch emit the target prediction; each round commits the
+ * accepted prefix plus that bonus token) and Tree Verification and DDTree
+ * (the accepted root-to-leaf prefix is selected according to the target).
+ * Per tree s: start at the root; while some child c of the current node has
+ * token[c] == argmax_idx[current], move to the lowest-index such child.
+ * L_s = number of moves; bonus_s = argmax_idx[last node]; tau = L_s + 1.
+ *   node_offsets host int32 [S+1] (as in dt_attn_desc), read during the call
+ *   parent, token, argmax_idx  device int32 [N] (parent and path tree-local;
+ *              argmax_idx typically dt_argmax_rows' output)
+ *   path       device int32 [N]: path[node_offsets[s] + t], t = 0..L_s, is the
+ *              t-th accepted node (t = 0 is the root); the tree's other
+ *              entries are set to -1
+ *   accept_len device int32 [S] (L_s); bonus device int32 [S]
+ * Contract: parent as in the tree representation (a cycle-free walk is
+ * guaranteed regardless: the walk only moves to higher indices).
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_HIP.
+ */
+int dt_accept_path(int32_t num_seqs, const int32_t* node_offsets, const int32_t* parent, const int32_t* token,
+                   const int32_t* argmax_idx, int32_t* path, int32_t* accept_len, int32_t* bonus, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTREE_H */

@@ -1,0 +1,229 @@
+"""GPU parity of dt_tree_attention against the oracle (fp64, dense ancestor mask).
+
+Tolerance (attention output, bf16): max |got - ref| <= 2e-2 and, per (node,
+head) row, max |got - ref| / max |ref| <= 1e-2. Mask behaviour is also checked
+bit-exactly: perturbing the K/V of a node's non-ancestors leaves its output
+bits unchanged, and repeated runs give identical bits.
+"""
+
+import numpy as np
+import pytest
+
+import draft_tree_verification_dt_amd as dt
+from _helpers import assert_attention_close, dev_bf16, dev_i32, host_f64, require_gpu, tree, workload_inputs
+from gen import configs as gconf, rng as grng, tensors as gten
+from oracle import attention as oatt, tree as otree
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ops, parents, nodes, plens, Hq, Hkv, d, scale=None, split_keys=0, prefix=None, layout=None):
+    """Run dt_tree_attention on packed host operands; returns (out tensor, device inputs)."""
+    import torch
+
+    q, kt, vt = dev_bf16(ops["q"]), dev_bf16(ops["k_tree"]), dev_bf16(ops["v_tree"])
+    if prefix is None:
+        kp = dev_bf16(ops["k_prefix"]) if ops["k_prefix"].shape[0] else None
+        vp = dev_bf16(ops["v_prefix"]) if ops["v_prefix"].shape[0] else None
+    else:
+        kp, vp = prefix
+    par = dev_i32(np.concatenate(parents))
+    if layout is None:
+        layout = dt.AttnLayout(np.concatenate([[0], np.cumsum(nodes)]), plens)
+    out = dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, scale=scale, split_keys=split_keys)
+    torch.cuda.synchronize()
+    return out, (q, kt, vt, kp, vp, par, layout)
+
+
+def _oracle(ops, parents, nodes, plens, scale=None):
+    offs = np.concatenate([[0], np.cumsum(nodes)])
+    starts = np.concatenate([[0], np.cumsum(plens)[:-1]]).astype(np.int64)
+    return oatt.batch_tree_attention(ops["q"], ops["k_tree"], ops["v_tree"], ops["k_prefix"], ops["v_prefix"],
+                                     np.concatenate(parents), offs, plens, starts, scale)
+
+
+def _case(nodes, plens, Hq, Hkv, d, shapes, seed, scale=None):
+    r = grng.stream(seed, "gpu-att")
+    parents = [tree(shapes[i % len(shapes)], n, seed * 31 + i)[0] for i, n in enumerate(nodes)]
+    ops = [gten.attention_operands(r, n, P, Hq, Hkv, d, scale=scale) for n, P in zip(nodes, plens)]
+    return parents, {k: np.concatenate([o[k] for o in ops]) for k in ops[0]}
+
+
+def test_tiny_config():
+    require_gpu()
+    w = gconf.tiny()
+    parents, tokens, ops = workload_inputs(w)
+    print("tiny: n=16 P=128 d=64 Hq=Hkv=1", flush=True)
+    out, _ = _run(ops, parents, w.nodes, w.prefix_lens, w.Hq, w.Hkv, w.d)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, w.nodes, w.prefix_lens), what="tiny")
+
+
+EDGE_N = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 512]
+
+
+@pytest.mark.parametrize("P", [0, 1, 63, 64, 65])
+@pytest.mark.parametrize("n", EDGE_N)
+def test_edge_shapes_d128_g4(P, n):
+    require_gpu()
+    parents, ops = _case([n], [P], 8, 2, 128, ["recursive", "deep", "bfs"], seed=P * 1000 + n)
+    print(f"edge d=128 g=4 P={P} n={n}", flush=True)
+    out, _ = _run(ops, parents, [n], [P], 8, 2, 128)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"P={P} n={n}")
+
+
+@pytest.mark.parametrize("P,n", [(0, 1), (1, 17), (65, 64), (200, 129), (64, 512)])
+def test_edge_shapes_d64_g1(P, n):
+    require_gpu()
+    parents, ops = _case([n], [P], 2, 2, 64, ["deep"], seed=7 + P + n)
+    print(f"edge d=64 g=1 P={P} n={n}", flush=True)
+    out, _ = _run(ops, parents, [n], [P], 2, 2, 64)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"d64 P={P} n={n}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 8])
+def test_group_sizes(g):
+    require_gpu()
+    parents, ops = _case([40], [150], 2 * g, 2, 128, ["recursive"], seed=90 + g)
+    print(f"gqa g={g}", flush=True)
+    out, _ = _run(ops, parents, [40], [150], 2 * g, 2, 128)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [40], [150]), what=f"g={g}")
+
+
+def test_sharp_distribution_and_custom_scale():
+    require_gpu()
+    parents, ops = _case([100], [300], 8, 2, 128, ["deep"], seed=5, scale=1.0)
+    print("sharp", flush=True)
+    out, _ = _run(ops, parents, [100], [300], 8, 2, 128)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [100], [300]), what="sharp")
+    out2, _ = _run(ops, parents, [100], [300], 8, 2, 128, scale=0.05)
+    assert_attention_close(host_f64(out2), _oracle(ops, parents, [100], [300], scale=0.05), what="scale")
+
+
+@pytest.mark.parametrize("split", [64, 128, 576, 4096])
+def test_forced_key_splits(split):
+    require_gpu()
+    parents, ops = _case([100], [1000], 8, 2, 128, ["deep"], seed=11, scale=0.5)
+    print(f"split_keys={split}", flush=True)
+    out, _ = _run(ops, parents, [100], [1000], 8, 2, 128, split_keys=split)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [100], [1000]), what=f"split {split}")
+
+
+def test_ragged_batch_strided_cache():
+    """Five sequences with different prefixes and trees; the prefix cache is
+    head-major [Hkv][rows][d] with gaps between the sequences' rows."""
+    import torch
+
+    require_gpu()
+    nodes, plens = [1, 33, 100, 256, 17], [0, 17, 500, 1000, 64]
+    Hq, Hkv, d = 8, 2, 128
+    parents, ops = _case(nodes, plens, Hq, Hkv, d, ["deep", "recursive", "bfs", "heap", "chain"], seed=21, scale=0.6)
+    gap = 37
+    starts = []
+    row = 5
+    for P in plens:
+        starts.append(row)
+        row += P + gap
+    cache_rows = row
+    kc = torch.zeros((Hkv, cache_rows, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    src = 0
+    for P, st in zip(plens, starts):
+        kc[:, st:st + P] = dev_bf16(ops["k_prefix"][src:src + P]).transpose(0, 1)
+        vc[:, st:st + P] = dev_bf16(ops["v_prefix"][src:src + P]).transpose(0, 1)
+        src += P
+    kp = kc.transpose(0, 1)  # [rows][Hkv][d] view: row stride d, head stride rows*d
+    vp = vc.transpose(0, 1)
+    layout = dt.AttnLayout(np.concatenate([[0], np.cumsum(nodes)]), plens, starts)
+    print("ragged strided", flush=True)
+    out, _ = _run(ops, parents, nodes, plens, Hq, Hkv, d, prefix=(kp, vp), layout=layout)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, nodes, plens), what="ragged")
+
+
+def test_many_sequences_multi_launch():
+    """More sequences than one launch carries."""
+    require_gpu()
+    rng = grng.stream(3, "many")
+    nodes = [int(x) for x in rng.integers(1, 40, size=70)]
+    plens = [int(x) for x in rng.integers(0, 130, size=70)]
+    parents, ops = _case(nodes, plens, 4, 1, 64, ["recursive", "deep"], seed=33)
+    print("70 sequences", flush=True)
+    out, _ = _run(ops, parents, nodes, plens, 4, 1, 64)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, nodes, plens), what="many")
+
+
+def test_non_ancestor_perturbation_bit_exact_and_determinism():
+    import torch
+
+    require_gpu()
+    n, P = 200, 300
+    parents, ops = _case([n], [P], 8, 2, 128, ["recursive"], seed=41)
+    print("perturbation", flush=True)
+    base, _ = _run(ops, parents, [n], [P], 8, 2, 128)
+    again, _ = _run(ops, parents, [n], [P], 8, 2, 128)
+    assert torch.equal(base, again), "two runs differ"
+    anc = otree.ancestor_matrix(parents[0])
+    rng = grng.stream(42)
+    for i in [0, 1, 57, 150, 199]:
+        others = ~anc[i]
+        ops2 = dict(ops)
+        for key in ("k_tree", "v_tree"):
+            a = ops[key].copy()
+            sign = np.where(rng.random(int(others.sum())) < 0.5, -1.0, 1.0).astype(np.float32)[:, None, None]
+            a[others] = gten.bf16_round(a[others] + np.float32(500.0) * sign)
+            ops2[key] = a
+        pert, _ = _run(ops2, parents, [n], [P], 8, 2, 128)
+        assert torch.equal(pert[i], base[i]), f"node {i} saw a non-ancestor"
+        if others.any():
+            assert not torch.equal(pert, base)
+
+
+@pytest.mark.parametrize("name", ["b128", "b256", "chain16"])
+def test_full_size_single_sequence(name):
+    """Qwen3-4B-shaped layers (Hq=32, Hkv=8, d=128) at full size, whole output."""
+    require_gpu()
+    w = gconf.get(name)
+    parents, tokens, ops = workload_inputs(w)
+    print(f"full {w.name}", flush=True)
+    out, _ = _run(ops, parents, w.nodes, w.prefix_lens, w.Hq, w.Hkv, w.d)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, w.nodes, w.prefix_lens), what=w.name)
+
+
+def test_full_size_ragged_batch():
+    require_gpu()
+    w = gconf.ragged()
+    parents, tokens, ops = workload_inputs(w)
+    print(f"full {w.name} P={w.prefix_lens}", flush=True)
+    out, _ = _run(ops, parents, w.nodes, w.prefix_lens, w.Hq, w.Hkv, w.d)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, w.nodes, w.prefix_lens), what=w.name)
+
+
+def test_long_context_sampled_rows():
+    """4 x (P=32768, n=512): operands drawn on the device, 96 sampled
+    (sequence, node, head) rows checked against the oracle's per-row form."""
+    import torch
+
+    require_gpu()
+    w = gconf.long_context()
+    Hq, Hkv, d = w.Hq, w.Hkv, w.d
+    N, PT = w.total_nodes, w.total_prefix
+    sc = 1.0 / np.sqrt(d)
+    q = gten.device_randn_bf16((N, Hq, d), w.seed, "q", scale=sc)
+    kt = gten.device_randn_bf16((N, Hkv, d), w.seed, "kt", scale=sc)
+    vt = gten.device_randn_bf16((N, Hkv, d), w.seed, "vt", scale=sc)
+    kp = gten.device_randn_bf16((PT, Hkv, d), w.seed, "kp", scale=sc)
+    vp = gten.device_randn_bf16((PT, Hkv, d), w.seed, "vp", scale=sc)
+    parents = [tree("heap", n, w.seed * 1000 + s)[0] for s, n in enumerate(w.nodes)]
+    layout = dt.AttnLayout(w.node_offsets(), w.prefix_lens)
+    print(f"long {w.name}", flush=True)
+    out = dt.dt_tree_attention(q, kt, vt, kp, vp, dev_i32(np.concatenate(parents)), layout)
+    torch.cuda.synchronize()
+    hq, hkt, hvt, hout = (host_f64(t) for t in (q, kt, vt, out))
+    rng = grng.stream(w.seed, "rows")
+    offs, starts = w.node_offsets(), w.prefix_row_starts()
+    for s in range(w.num_seqs):
+        a, b, p0, P = offs[s], offs[s + 1], starts[s], w.prefix_lens[s]
+        hkp, hvp = host_f64(kp[p0:p0 + P]), host_f64(vp[p0:p0 + P])
+        rows = [(int(rng.integers(0, b - a)), int(rng.integers(0, Hq))) for _ in range(24)]
+        ref = oatt.tree_attention_rows(hq[a:b], hkt[a:b], hvt[a:b], hkp, hvp, parents[s], rows)
+        got = np.stack([hout[a + i, h] for i, h in rows])
+        assert_attention_close(got, ref, what=f"long seq {s}")
