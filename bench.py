@@ -1,0 +1,335 @@
+"""Benchmark: one draft-tree verification round per step, on one MI355X.
+
+A step runs the whole verification path over one synthetic round:
+  1. dt_build_tree      best-first tree from this round's per-depth candidates (host)
+  2. upload parent/token (pinned host -> HBM, async)
+  3. dt_tree_attention  x L layers, each with its own KV cache
+  4. dt_argmax_rows     greedy prediction at every node over the full vocabulary
+  5. dt_accept_path     accepted path, length and bonus token
+Inputs (KV caches, Q/K/V of the tree, logits) are resident in HBM before the
+timed region; only the tree itself is built per step, as a round would.
+
+Default workload: Qwen3-4B-shaped target (32 query heads, 8 KV heads, head dim
+128, 36 layers, vocabulary 151936), one sequence with an 8192-token verified
+prefix and a 256-node tree. Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify TFLOP/s + % MFMA/HBM roofline; us per round at B=256"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+N_TABLES = 4  # distinct draft-candidate tables cycled through the steps
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="round", help="gen.configs name (round, b128, b256, chain16, ragged, long)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+class Round:
+    """Device-resident inputs of one workload and the launches of one step."""
+
+    def __init__(self, w, device):
+        import torch
+
+        import draft_tree_verification_dt_amd as dt
+        from gen import draft as gdraft, rng as grng, tensors as gten
+
+        self.w, self.dt, self.torch = w, dt, torch
+        self.dev = device
+        S, Hq, Hkv, d, L = w.num_seqs, w.Hq, w.Hkv, w.d, w.layers
+        N, PT = w.total_nodes, w.total_prefix
+        sc = 1.0 / np.sqrt(d)
+        self.offs = w.node_offsets()
+        self.layout = dt.AttnLayout(self.offs, w.prefix_lens, w.prefix_row_starts())
+        # per-layer operands; every layer has its own KV cache
+        self.kp = [gten.device_randn_bf16((PT, Hkv, d), w.seed, "kp", l, scale=sc) for l in range(L)]
+        self.vp = [gten.device_randn_bf16((PT, Hkv, d), w.seed, "vp", l, scale=sc) for l in range(L)]
+        self.q = [gten.device_randn_bf16((N, Hq, d), w.seed, "q", l, scale=sc) for l in range(L)]
+        self.kt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "kt", l, scale=sc) for l in range(L)]
+        self.vt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "vt", l, scale=sc) for l in range(L)]
+        self.out = [torch.empty((N, Hq, d), dtype=torch.bfloat16, device=device) for _ in range(L)]
+
+        # per-round draft candidates (host) and the planted target logits that go with them
+        self.tables = []
+        self.logits = []
+        self.trees = []
+        for t in range(N_TABLES):
+            per_seq = []
+            for s, n in enumerate(w.nodes):
+                r = grng.stream(w.seed, "cand", t, s)
+                lp, tok = gdraft.candidates(r, depths=w.depths, vocab=w.vocab, k=w.cand_k(n))
+                per_seq.append((lp, tok, int(r.integers(0, w.vocab)), n))
+            self.tables.append(per_seq)
+            trees = [dt.dt_build_tree(lp, tok, root, n, with_score=False) for lp, tok, root, n in per_seq]
+            self.trees.append(trees)
+            lg = gten.device_logits(N, w.vocab, w.seed, "logits", t)
+            for s, (p, tk, _, _) in enumerate(trees):
+                gten.device_plant(grng.stream(w.seed, "plant", t, s), lg, int(self.offs[s]), p, tk, p=w.plant_p)
+            self.logits.append(lg)
+
+        # tree upload buffers (pinned host, double-buffered) and device copies
+        self.h_tree = [torch.empty((2, N), dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.d_tree = torch.empty((2, N), dtype=torch.int32, device=device)
+        self.am = torch.empty(N, dtype=torch.int32, device=device)
+        self.path = torch.empty(N, dtype=torch.int32, device=device)
+        self.acc = torch.empty(S, dtype=torch.int32, device=device)
+        self.bonus = torch.empty(S, dtype=torch.int32, device=device)
+        ws_att = dt.dt_tree_attention_workspace_size(self.q[0], self.kt[0], self.kp[0], self.layout)
+        self.ws_att = torch.empty(max(ws_att, 256), dtype=torch.uint8, device=device)
+        ws_am = dt.dt_argmax_rows_workspace_size(N, w.vocab)
+        self.ws_am = torch.empty(max(ws_am, 256), dtype=torch.uint8, device=device)
+        self.upload_done = [None, None]
+        self._prepare_raw_calls()
+        self.step_idx = 0
+
+    def _prepare_raw_calls(self):
+        """Marshal the per-layer C-ABI arguments once (the timed loop then only
+        issues the calls)."""
+        import ctypes
+
+        from draft_tree_verification_dt_amd import _lib
+
+        dt, w = self.dt, self.w
+        self.lib = _lib.load()
+        self.desc = dt._attn_geometry(self.q[0], self.kt[0], self.kp[0], self.layout, None, 0)
+        self.desc.out_row_stride = self.out[0].stride(0)
+        self.desc_ref = ctypes.byref(self.desc)
+        self.stream = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        self.att_args = [(self.q[l].data_ptr(), self.kt[l].data_ptr(), self.vt[l].data_ptr(), self.kp[l].data_ptr(),
+                          self.vp[l].data_ptr(), self.d_tree[0].data_ptr(), self.out[l].data_ptr(),
+                          self.ws_att.data_ptr(), self.ws_att.numel()) for l in range(w.layers)]
+        self.offs_c = np.ascontiguousarray(self.offs, dtype=np.int32)
+        self.offs_ptr = self.offs_c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def build_and_upload(self):
+        t = self.step_idx % N_TABLES
+        slot = self.step_idx % 2
+        if self.upload_done[slot] is not None:
+            self.upload_done[slot].synchronize()  # the pinned slot's previous copy has finished
+        h = self.h_tree[slot]
+        for s, (lp, tok, root, n) in enumerate(self.tables[t]):
+            p, tk, _, _ = self.dt.dt_build_tree(lp, tok, root, n, with_score=False)
+            a = int(self.offs[s])
+            h[0, a:a + n] = self.torch.from_numpy(p)
+            h[1, a:a + n] = self.torch.from_numpy(tk)
+        self.d_tree.copy_(h, non_blocking=True)
+        ev = self.torch.cuda.Event()
+        ev.record()
+        self.upload_done[slot] = ev
+        return t
+
+    def attention(self, l):
+        st = self.lib.dt_tree_attention(self.desc_ref, *self.att_args[l], self.stream)
+        if st != 0:
+            raise self.dt.DtError(st, "dt_tree_attention")
+
+    def step(self):
+        t = self.build_and_upload()
+        for l in range(self.w.layers):
+            self.attention(l)
+        lg = self.logits[t]
+        st = self.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), self.am.data_ptr(),
+                                     self.ws_am.data_ptr(), self.ws_am.numel(), self.stream)
+        if st != 0:
+            raise self.dt.DtError(st, "dt_argmax_rows")
+        st = self.lib.dt_accept_path(self.w.num_seqs, self.offs_ptr, self.d_tree[0].data_ptr(),
+                                     self.d_tree[1].data_ptr(), self.am.data_ptr(), self.path.data_ptr(),
+                                     self.acc.data_ptr(), self.bonus.data_ptr(), self.stream)
+        if st != 0:
+            raise self.dt.DtError(st, "dt_accept_path")
+        self.step_idx += 1
+
+    def attention_flops(self, table):
+        """Algorithmic flops of one layer for the trees of `table` (ancestor pairs only)."""
+        from oracle.attention import flops
+
+        return flops(self.w.nodes, self.w.prefix_lens, [p for p, _, _, _ in self.trees[table]], self.w.Hq, self.w.d)
+
+
+def time_attention_calls(rnd, reps):
+    """Average duration of one dt_tree_attention call, from HIP events recorded
+    on the stream the kernels run on."""
+    torch = rnd.torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        rnd.attention(i % rnd.w.layers)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)), float(np.median(ms))
+
+
+def time_argmax_calls(rnd, reps):
+    torch = rnd.torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        lg = rnd.logits[i % N_TABLES]
+        evs[i][0].record()
+        rnd.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), rnd.am.data_ptr(),
+                               rnd.ws_am.data_ptr(), rnd.ws_am.numel(), rnd.stream)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def parity_check(rnd):
+    """Re-check the timed path against the oracle: sampled attention rows of
+    layer 0 and the whole argmax / walk of the last step's table."""
+    from oracle import argmax as oarg, attention as oatt, walk as owalk
+
+    torch, w = rnd.torch, rnd.w
+    torch.cuda.synchronize()
+    t = (rnd.step_idx - 1) % N_TABLES
+    f = lambda x: x.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for s in range(w.num_seqs):
+        a, b = int(rnd.offs[s]), int(rnd.offs[s + 1])
+        p0, P = int(w.prefix_row_starts()[s]), w.prefix_lens[s]
+        parent = rnd.trees[t][s][0]
+        rows = [(int(rng.integers(0, b - a)), int(rng.integers(0, w.Hq))) for _ in range(16)]
+        ref = oatt.tree_attention_rows(f(rnd.q[0][a:b]), f(rnd.kt[0][a:b]), f(rnd.vt[0][a:b]), f(rnd.kp[0][p0:p0 + P]),
+                                       f(rnd.vp[0][p0:p0 + P]), parent, rows)
+        got = np.stack([f(rnd.out[0][a + i, h]) for i, h in rows])
+        err = np.abs(got - ref).max(-1) / np.abs(ref).max(-1)
+        worst = max(worst, float(err.max()))
+    am_ref = oarg.argmax_rows(rnd.logits[t].cpu().numpy())
+    am_ok = bool(np.array_equal(rnd.am.cpu().numpy(), am_ref))
+    walks = owalk.batch_accept_path(np.concatenate([x[0] for x in rnd.trees[t]]),
+                                    np.concatenate([x[1] for x in rnd.trees[t]]), am_ref, rnd.offs)
+    acc, bon = rnd.acc.cpu().numpy(), rnd.bonus.cpu().numpy()
+    walk_ok = all(int(acc[s]) == L and int(bon[s]) == bo for s, (_, L, bo) in enumerate(walks))
+    return {"attention_row_rel_err_max": worst, "argmax_exact": am_ok, "walk_exact": walk_ok,
+            "mean_accept_len": float(np.mean([L for _, L, _ in walks]))}
+
+
+def cpu_baseline(rnd, budget_s):
+    """The oracle, as it is, on this host's cores: a bounded sample of the same
+    round (some of the layers' attention, plus argmax, walk and tree build),
+    scaled to a full round."""
+    from oracle import argmax as oarg, attention as oatt, build_tree as obt, walk as owalk
+
+    w, torch = rnd.w, rnd.torch
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    f = lambda x: x.float().cpu().numpy()  # noqa: E731
+    t = 0
+    t0 = time.perf_counter()
+    trees = [obt.build_tree_heap(lp, tok, root, n) for lp, tok, root, n in rnd.tables[t]]
+    t_build = time.perf_counter() - t0
+    parents = [np.array(x[0]) for x in trees]
+    starts = w.prefix_row_starts()
+    layer_times = []
+    spent = 0.0
+    for l in range(w.layers):
+        args = [f(x[l]) for x in (rnd.q, rnd.kt, rnd.vt, rnd.kp, rnd.vp)]
+        t0 = time.perf_counter()
+        oatt.batch_tree_attention(*args, np.concatenate(parents), rnd.offs, w.prefix_lens, starts)
+        layer_times.append(time.perf_counter() - t0)
+        spent += layer_times[-1]
+        if spent > budget_s and len(layer_times) >= 1:
+            break
+    lg = rnd.logits[t].cpu().numpy()
+    t0 = time.perf_counter()
+    am = oarg.argmax_rows(lg)
+    t_arg = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    owalk.batch_accept_path(np.concatenate(parents), np.concatenate([x[1] for x in trees]), am, rnd.offs)
+    t_walk = time.perf_counter() - t0
+    round_s = t_build + np.mean(layer_times) * w.layers + t_arg + t_walk
+    flops = rnd.attention_flops(t) * w.layers
+    return {
+        "value": flops / round_s / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas_threads) if blas_threads else cores),
+        "kind": "oracle",
+        "sample": f"{len(layer_times)} of {w.layers} layers' attention timed (numpy float64, dense ancestor mask), "
+                  f"plus tree build, argmax and walk once; scaled to one full round",
+        "us_per_round": round_s * 1e6, "host_cores_visible": cores, "blas_threads": blas_threads,
+        "seconds": {"build": t_build, "attention_per_layer": float(np.mean(layer_times)), "argmax": t_arg, "walk": t_walk},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification path of one round is "
+              "single-GPU here, see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from gen import configs as gconf
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = gconf.get(args.workload)
+    rnd = Round(w, dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        rnd.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rnd.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    flops_layer = float(np.mean([rnd.attention_flops(t) for t in range(N_TABLES)]))
+    round_flops = flops_layer * w.layers
+    value = round_flops / (ms_per_step / 1e3) / 1e12
+
+    parity = None if args.no_parity else parity_check(rnd)  # checks the last timed step's outputs
+    att_mean_ms, att_med_ms = time_attention_calls(rnd, reps=max(2 * w.layers, 36))
+    arg_ms = time_argmax_calls(rnd, reps=10)
+    achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
+    argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
+
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "prefix_lens": w.prefix_lens if w.num_seqs <= 8 else "ragged",
+                   "tree_nodes": w.nodes[0] if len(set(w.nodes)) == 1 else w.nodes, "layers": w.layers,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "vocab": w.vocab, "tree": w.tree},
+        "us_per_round": round(ms_per_step * 1e3, 1),
+        "roofline": {"bound": "mfma", "kernel": "dt_tree_attention (tree_attn_fwd + tree_attn_combine)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops_layer, "launch_ms_mean": att_mean_ms, "launch_ms_median": att_med_ms},
+        "argmax": {"ms": arg_ms, "GB/s": argmax_bytes / (arg_ms / 1e3) / 1e9,
+                   "frac_hbm": argmax_bytes / (arg_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(rnd, args.cpu_budget_s)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -103,66 +103,94 @@ __device__ inline int find_seq(const AttnParams& p, int item) {
 // 16-byte (8 x bf16) global load.
 __device__ inline uint4 ld16(const bf16_bits* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
 
-// LDS layouts (D = head dim), padded so that every operand read is a per-lane
-// base address plus a compile-time offset and the MFMA operand reads are free
-// of bank conflicts:
-//  K tile   [64 keys][D + 8]   (row pitch / 16 bytes is odd)
-//  V^T tile [D][64 + 4 keys]   (consecutive d rows start 8 bytes apart in bank space)
-template <int D> struct Lds {
-  static constexpr int kPitch = D + 8;
-  static constexpr int vPitch = kBN + 4;
-  static constexpr int kElems = kBN * kPitch;
-  static constexpr int vElems = D * vPitch;
+// LDS tiles (D = head dim, rows of D*2 bytes, no padding). A tile of 64 keys
+// of K and one of V per buffer, double-buffered. Rows are XOR-swizzled at
+// 16-byte-chunk granularity so that the MFMA operand reads are free of bank
+// conflicts while every lane's swizzle stays constant across the tile:
+//   K: logical chunk c of row r sits at chunk c ^ (r & 7)
+//   V: logical chunk c of row r sits at chunk c ^ (2 * (r & 3))
+// Tiles are filled straight from global memory with global_load_lds_dwordx4
+// (each wave instruction writes 1 KB of consecutive LDS; the lane picks the
+// global chunk that belongs at its swizzled slot), so no registers stage them.
+template <int D>
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;  // rows one wave instruction fills
+  static constexpr int kInstrPerWave = kBN / kRowsPerInstr / 4;
+  static constexpr int kBytes = kBN * kRowBytes;          // one K (or V) tile
 };
 
-template <int D>
-struct TileLoader {
-  // Each thread moves 4 (D=128) or 2 (D=64) 16-byte chunks of K and of V per tile.
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kIters = kBN * kChunksPerRow / kThreads;
-  uint4 kreg[kIters];
-  uint4 vreg[kIters];
+__device__ inline int k_swz(int r) { return r & 7; }
+__device__ inline int v_swz(int r) { return 2 * (r & 3); }
 
-  // Address of key `key` (sequence-local; prefix rows first, then tree nodes).
-  __device__ inline void load(const AttnParams& p, const SeqGeom& sg, int head, int kb, int key_end, int tid) {
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// Issue the loads of one K tile and one V tile (keys kb .. kb+63) into LDS,
+// general form: each row may come from the prefix cache or from the tree's own
+// K/V. Keys at or beyond key_end are read from row key_end-1 instead (always
+// valid; those keys are masked out, so their values only need to be finite).
+template <int D>
+__device__ inline void issue_tile(const AttnParams& p, const SeqGeom& sg, int head, int kb, int key_end,
+                                  char* kbuf, char* vbuf, int wave, int lane) {
+  using T = Tile<D>;
+  const int rsub = lane / T::kChunks;  // row within the instruction's rows
+  const int pc = lane % T::kChunks;    // physical chunk this lane fills
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int idx = tid + it * kThreads;
-      const int r = idx / kChunksPerRow;
-      const int c = idx % kChunksPerRow;
-      const int key = kb + r;
-      if (key < key_end) {
-        const bf16_bits *kptr, *vptr;
-        if (key < sg.P) {
-          const int64_t off = (sg.prefix_row0 + key) * p.p_rs + head * p.p_hs + c * 8;
-          kptr = p.kp + off;
-          vptr = p.vp + off;
-        } else {
-          const int64_t off = (int64_t)(sg.node_off + key - sg.P) * p.t_rs + head * D + c * 8;
-          kptr = p.kt + off;
-          vptr = p.vt + off;
-        }
-        kreg[it] = ld16(kptr);
-        vreg[it] = ld16(vptr);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
-      }
+  for (int i = 0; i < T::kInstrPerWave; ++i) {
+    const int instr = wave * T::kInstrPerWave + i;
+    const int row = instr * T::kRowsPerInstr + rsub;
+    int key = kb + row;
+    key = key < key_end ? key : key_end - 1;
+    int64_t base;
+    const bf16_bits *kb_ptr, *vb_ptr;
+    if (key < sg.P) {
+      base = (sg.prefix_row0 + key) * p.p_rs + (int64_t)head * p.p_hs;
+      kb_ptr = p.kp;
+      vb_ptr = p.vp;
+    } else {
+      base = (int64_t)(sg.node_off + key - sg.P) * p.t_rs + (int64_t)head * D;
+      kb_ptr = p.kt;
+      vb_ptr = p.vt;
+    }
+    const bf16_bits* ksrc = kb_ptr + base + ((pc ^ k_swz(row)) << 3);
+    const bf16_bits* vsrc = vb_ptr + base + ((pc ^ v_swz(row)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_ptr)(kbuf + instr * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_ptr)(vbuf + instr * 1024), 16, 0, 0);
+  }
+}
+
+// Fast form for tiles that lie wholly inside the prefix: one wave-uniform base
+// address per tile plus per-lane 32-bit byte offsets fixed for the whole loop.
+template <int D>
+struct PrefixLoads {
+  using T = Tile<D>;
+  uint32_t koff[T::kInstrPerWave];
+  uint32_t voff[T::kInstrPerWave];
+
+  __device__ inline void init(int64_t row_stride, int wave, int lane) {
+    const int rsub = lane / T::kChunks, pc = lane % T::kChunks;
+#pragma unroll
+    for (int i = 0; i < T::kInstrPerWave; ++i) {
+      const int row = (wave * T::kInstrPerWave + i) * T::kRowsPerInstr + rsub;
+      const uint32_t roff = (uint32_t)(row * row_stride * 2);
+      koff[i] = roff + ((pc ^ k_swz(row)) << 4);
+      voff[i] = roff + ((pc ^ v_swz(row)) << 4);
     }
   }
 
-  __device__ inline void store(bf16_bits* ks, bf16_bits* vts, int tid) {
+  __device__ inline void issue(const AttnParams& p, const SeqGeom& sg, int head, int kb, char* kbuf, char* vbuf,
+                               int wave) const {
+    const int64_t first = ((sg.prefix_row0 + kb) * p.p_rs + (int64_t)head * p.p_hs) * 2;
+    const char* kbase = reinterpret_cast<const char*>(p.kp) + first;
+    const char* vbase = reinterpret_cast<const char*>(p.vp) + first;
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int idx = tid + it * kThreads;
-      const int r = idx / kChunksPerRow;
-      const int c = idx % kChunksPerRow;
-      *reinterpret_cast<uint4*>(ks + r * Lds<D>::kPitch + c * 8) = kreg[it];
-      // V^T: the 8 values of key r, dims c*8 .. c*8+7, go to 8 different rows.
-      const bf16_bits* v = reinterpret_cast<const bf16_bits*>(&vreg[it]);
-      bf16_bits* dst = vts + (c * 8) * Lds<D>::vPitch + r;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j * Lds<D>::vPitch] = v[j];
+    for (int i = 0; i < T::kInstrPerWave; ++i) {
+      const int instr = wave * T::kInstrPerWave + i;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + koff[i]), (lds_void_ptr)(kbuf + instr * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + voff[i]), (lds_void_ptr)(vbuf + instr * 1024), 16, 0, 0);
     }
   }
 };
@@ -175,12 +203,15 @@ __device__ inline uint64_t mask_bits(const uint32_t* row, int j0, int cnt) {
   return cnt >= 64 ? x : (x & ((1ull << cnt) - 1));
 }
 
+constexpr float kRescaleSlack = 8.f;  // log2 units a stale running max may lag the true one
+constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" for the running max
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p) {
+  using T = Tile<D>;
   constexpr int KS = D / 16;  // k-steps of the QK^T product
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim
-  __shared__ __attribute__((aligned(16))) bf16_bits ks[Lds<D>::kElems];
-  __shared__ __attribute__((aligned(16))) bf16_bits vts[Lds<D>::vElems];
+  __shared__ __attribute__((aligned(1024))) char tiles[2][2][T::kBytes];  // [buffer][K, V]
   extern __shared__ uint32_t dyn[];  // [max_n] parents, then [mask_rows][mask_words] ancestor masks
 
   // ---- work item (XCD-aware remap: consecutive items share an XCD) ----
@@ -217,6 +248,17 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   key_hi = min(key_hi, sg.P + node_hi + 1);  // later tree keys are no one's ancestor here
   const int ntiles = key_hi > key_lo ? (key_hi - key_lo + kBN - 1) / kBN : 0;
 
+  // tiles below this key are wholly prefix and take the fast load path
+  const int fast_end = min(sg.P, key_hi);
+  PrefixLoads<D> pl;
+  pl.init(p.p_rs, wave, lane);
+  if (ntiles > 0) {
+    if (key_lo + kBN <= fast_end)
+      pl.issue(p, sg, head, key_lo, tiles[0][0], tiles[0][1], wave);
+    else
+      issue_tile<D>(p, sg, head, key_lo, key_hi, tiles[0][0], tiles[0][1], wave, lane);
+  }
+
   uint32_t* par_s = dyn;
   uint32_t* masks = dyn + p.max_n;
 
@@ -237,10 +279,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         j = pj;
       }
     }
-    __syncthreads();
   }
 
-  // ---- Q rows as the B operand of S^T = K Q^T: lane holds row lr, dims ks*16 + hh*8 .. +7 ----
+  // ---- Q rows as the B operand of S^T = K Q^T: lane holds row lr, dims 16k + 8hh .. +7 ----
   bf16x8 qreg[KS];
   {
     const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
@@ -256,47 +297,49 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
-  float m_run = -INFINITY;  // running max (log2 units), identical in both half-waves
-  float l_run = 0.f;        // running sum over this half-wave's keys
-
-  TileLoader<D> ld;
-  if (ntiles > 0) {
-    ld.load(p, sg, head, key_lo, key_hi, tid);
-    ld.store(ks, vts, tid);
-    __syncthreads();
-  }
+  float m_run = kInitMax;  // running max (log2 units; may lag the true max by < kRescaleSlack)
+  float l_run = 0.f;       // running sum over this half-wave's keys
+  const float c = p.scale_log2;
   const int prefix_end = min(sg.P, key_hi);  // keys below this are visible to every row
   const uint32_t* my_mask = masks + (my_node - node_lo) * p.mask_words;
 
+  // per-lane LDS byte offsets of the operand reads
+  const int k_off = lr * T::kRowBytes;                       // + chunk, see below
+  const int s16 = lane & 15, grp = lane >> 4;
+  const int v_row = hh * 4 + (s16 >> 2);                     // + 32bb + 16sub + 8hi
+  const int v_chunk_lo = (grp & 1) * 2 + ((s16 & 3) >> 1);    // + 4db, then swizzled
+  const int v_in = (s16 & 1) * 8;
+
   for (int t = 0; t < ntiles; ++t) {
     const int kb = key_lo + t * kBN;
+    const int cur = t & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile t have landed (vmcnt = 0)
+    __syncthreads();                     // everyone's have; everyone is done with tile t-1
+    if (t + 1 < ntiles) {
+      if (kb + 2 * kBN <= fast_end)
+        pl.issue(p, sg, head, kb + kBN, tiles[cur ^ 1][0], tiles[cur ^ 1][1], wave);
+      else
+        issue_tile<D>(p, sg, head, kb + kBN, key_hi, tiles[cur ^ 1][0], tiles[cur ^ 1][1], wave, lane);
+    }
+    const char* kt = tiles[cur][0];
+    const char* vt = tiles[cur][1];
 
-    // S^T block b (keys kb + 32b ..): lane (lr, hh) gets keys 32b + 8(i/4) + 4hh + (i%4), i = 0..15
+    // S^T block bb (keys kb + 32bb ..): lane (lr, hh) gets keys 32bb + 8(j/4) + 4hh + (j%4), j = 0..15
     f32x16 sc[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) sc[bb][j] = 0.f;
-      const bf16_bits* kbase = ks + (bb * 32 + lr) * Lds<D>::kPitch + hh * 8;
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + k * 16);
+        const int chunk = (2 * k + hh) ^ k_swz(lr);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + bb * 32 * T::kRowBytes + k_off + chunk * 16);
         sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[k], sc[bb], 0, 0, 0);
       }
     }
 
-    // ---- scale, mask, online softmax ----
-    float tmax = -INFINITY;
-    if (kb + kBN <= prefix_end) {
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          sc[bb][j] *= p.scale_log2;
-          tmax = fmaxf(tmax, sc[bb][j]);
-        }
-    } else {
-      // visibility of the 64 keys of this tile for my row
+    // ---- mask (tiles touching tree keys or the range end), then the running max ----
+    if (kb + kBN > prefix_end) {
       uint64_t vis = 0;
       const int npre = prefix_end - kb;
       if (npre > 0) vis = npre >= 64 ? ~0ull : ((1ull << npre) - 1);
@@ -307,53 +350,62 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int kk = bb * 32 + (j >> 2) * 8 + hh * 4 + (j & 3);
-          const float v = ((vis >> kk) & 1ull) ? sc[bb][j] * p.scale_log2 : -INFINITY;
-          sc[bb][j] = v;
-          tmax = fmaxf(tmax, v);
+          if (!((vis >> kk) & 1ull)) sc[bb][j] = -INFINITY;
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pb[2][2];
+    float mx = -INFINITY;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = __builtin_amdgcn_exp2f(sc[bb][j] - m_use);
-        psum += e;
-        pb[bb][j >> 3][j & 7] = (__bf16)e;
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sc[bb][j], sc[bb][j + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c;
+    // Rescale only when a row's max jumps by more than the slack (rare after
+    // the first tiles). The decision is per row, so a row's arithmetic depends
+    // on its own visible keys only; the branch is taken if any row needs it.
+    const bool need = mt > m_run + kRescaleSlack;
+    if (__any(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+    }
+    const float neg_m = -m_run;
+    bf16x8 pb[2][2];
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        bf16x2 pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][j], c, neg_m));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][j + 1], c, neg_m));
+        pb[bb][j >> 3][j & 7] = pr[0];
+        pb[bb][j >> 3][(j & 7) + 1] = pr[1];
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);  // sums the rounded probabilities
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
 
-    // ---- O^T += V^T P^T: k-slots of half hh <-> keys 32bb + 16sub + {4hh..4hh+3, 8+4hh..8+4hh+3} ----
-    const bf16_bits* vbase = vts + lr * Lds<D>::vPitch + hh * 4;
+    // ---- O^T += V^T P^T; V^T operands come from row-major V via transposing LDS reads ----
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
+      const int vch = ((i * 4 + v_chunk_lo) ^ (2 * (v_row & 3))) * 16 + v_in;
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const bf16_bits* vp = vbase + i * 32 * Lds<D>::vPitch + bb * 32 + sub * 16;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-          uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8*>(&a4), pb[bb][sub], acc[i], 0, 0, 0);
+          const char* vp0 = vt + (bb * 32 + sub * 16 + v_row) * T::kRowBytes + vch;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)vp0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vp0 + 8 * T::kRowBytes));
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&a8), pb[bb][sub],
+                                                             acc[i], 0, 0, 0);
         }
-    }
-
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      ld.load(p, sg, head, kb + kBN, key_hi, tid);
-      ld.store(ks, vts, tid);
-      __syncthreads();
     }
   }
 
@@ -412,7 +464,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   for (int k = 0; k < sg.splits; ++k) {
     const int64_t prow = (int64_t)sg.part_base + ((int64_t)k * sg.n + node) * p.Hq + qh;
     const float2 ml = p.part_ml[prow];
-    if (ml.x == -INFINITY) continue;  // chunk saw no visible key for this row
+    if (ml.y == 0.f) continue;  // chunk saw no visible key for this row
     const float w = __builtin_amdgcn_exp2f(ml.x - m);
     l += w * ml.y;
     const float* po = p.part_o + prow * D + lane * E;
@@ -459,6 +511,8 @@ int check_desc(const dt_attn_desc* d) {
   if (qrs < d->num_q_heads * D || ors < d->num_q_heads * D || trs < d->num_kv_heads * D) return DT_ERR_SHAPE;
   if (qrs % 8 || ors % 8 || trs % 8 || d->prefix_row_stride % 8 || d->prefix_head_stride % 8) return DT_ERR_SHAPE;
   if (d->prefix_row_stride < 0 || d->prefix_head_stride < 0) return DT_ERR_SHAPE;
+  // the kernel addresses 64 cache rows of a tile with 32-bit byte offsets
+  if (d->prefix_row_stride >= ((int64_t)1 << 24)) return DT_ERR_UNSUPPORTED;
   return DT_OK;
 }
 
