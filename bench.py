@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -286,6 +289,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src_buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr, flush=True)
+        del src_buf, dst_buf
     w = gconf.get(args.workload)
     rnd = Round(w, dev)
     torch.cuda.synchronize()
