@@ -55,6 +55,7 @@ constexpr int kBN = 64;         // keys per tile
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kMaxSeqs = 32;    // sequences per launch (host loops over larger batches)
 constexpr int kXcds = 8;
+constexpr int kMinTiles = 4;   // key tiles per work item at least (automatic split sizing)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SeqGeom {
@@ -107,8 +108,8 @@ __device__ inline uint4 ld16(const bf16_bits* ptr) { return *reinterpret_cast<co
 // of K and one of V per buffer, double-buffered. Rows are XOR-swizzled at
 // 16-byte-chunk granularity so that the MFMA operand reads are free of bank
 // conflicts while every lane's swizzle stays constant across the tile:
-//   K: logical chunk c of row r sits at chunk c ^ (r & 7)
-//   V: logical chunk c of row r sits at chunk c ^ (2 * (r & 3))
+//   K: logical chunk c of row r sits at chunk c ^ k_swz(r)
+//   V: logical chunk c of row r sits at chunk c ^ v_swz(r)
 // Tiles are filled straight from global memory with global_load_lds_dwordx4
 // (each wave instruction writes 1 KB of consecutive LDS; the lane picks the
 // global chunk that belongs at its swizzled slot), so no registers stage them.
@@ -121,8 +122,14 @@ struct Tile {
   static constexpr int kBytes = kBN * kRowBytes;          // one K (or V) tile
 };
 
-__device__ inline int k_swz(int r) { return r & 7; }
-__device__ inline int v_swz(int r) { return 2 * (r & 3); }
+// The LDS has 64 four-byte banks, i.e. a bank row of 256 bytes (one row of a
+// d = 128 tile, two rows of a d = 64 tile). The swizzles spread the 16 rows
+// read by one quarter-wave (K, 16-byte reads) and the 4 rows x 4 chunks read by
+// one half-wave (V, 8-byte transposing reads) over all 64 banks.
+template <int D>
+__device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -136,6 +143,13 @@ template <int D>
 __device__ inline void issue_tile(const AttnParams& p, const SeqGeom& sg, int head, int kb, int key_end,
                                   char* kbuf, char* vbuf, int wave, int lane) {
   using T = Tile<D>;
+  // The four base pointers as uniform values: selecting between them per lane
+  // must not turn into a per-lane load of the pointer (which would also wait
+  // for every load in flight).
+  const char* kp = reinterpret_cast<const char*>(p.kp);
+  const char* vp = reinterpret_cast<const char*>(p.vp);
+  const char* kt = reinterpret_cast<const char*>(p.kt);
+  const char* vt = reinterpret_cast<const char*>(p.vt);
   const int rsub = lane / T::kChunks;  // row within the instruction's rows
   const int pc = lane % T::kChunks;    // physical chunk this lane fills
 #pragma unroll
@@ -144,22 +158,22 @@ __device__ inline void issue_tile(const AttnParams& p, const SeqGeom& sg, int he
     const int row = instr * T::kRowsPerInstr + rsub;
     int key = kb + row;
     key = key < key_end ? key : key_end - 1;
-    int64_t base;
-    const bf16_bits *kb_ptr, *vb_ptr;
-    if (key < sg.P) {
-      base = (sg.prefix_row0 + key) * p.p_rs + (int64_t)head * p.p_hs;
-      kb_ptr = p.kp;
-      vb_ptr = p.vp;
-    } else {
-      base = (int64_t)(sg.node_off + key - sg.P) * p.t_rs + (int64_t)head * D;
-      kb_ptr = p.kt;
-      vb_ptr = p.vt;
-    }
-    const bf16_bits* ksrc = kb_ptr + base + ((pc ^ k_swz(row)) << 3);
-    const bf16_bits* vsrc = vb_ptr + base + ((pc ^ v_swz(row)) << 3);
+    const bool pre = key < sg.P;
+    const int64_t off = pre ? ((sg.prefix_row0 + key) * p.p_rs + (int64_t)head * p.p_hs) * 2
+                            : ((int64_t)(sg.node_off + key - sg.P) * p.t_rs + (int64_t)head * D) * 2;
+    const char* ksrc = (pre ? kp : kt) + off + ((pc ^ k_swz<D>(row)) << 4);
+    const char* vsrc = (pre ? vp : vt) + off + ((pc ^ v_swz<D>(row)) << 4);
     __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_ptr)(kbuf + instr * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_ptr)(vbuf + instr * 1024), 16, 0, 0);
   }
+}
+
+// A wave-uniform pointer, kept in scalar registers.
+__device__ inline const char* uniform_ptr(const char* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
 // Fast form for tiles that lie wholly inside the prefix: one wave-uniform base
@@ -176,16 +190,16 @@ struct PrefixLoads {
     for (int i = 0; i < T::kInstrPerWave; ++i) {
       const int row = (wave * T::kInstrPerWave + i) * T::kRowsPerInstr + rsub;
       const uint32_t roff = (uint32_t)(row * row_stride * 2);
-      koff[i] = roff + ((pc ^ k_swz(row)) << 4);
-      voff[i] = roff + ((pc ^ v_swz(row)) << 4);
+      koff[i] = roff + ((pc ^ k_swz<D>(row)) << 4);
+      voff[i] = roff + ((pc ^ v_swz<D>(row)) << 4);
     }
   }
 
   __device__ inline void issue(const AttnParams& p, const SeqGeom& sg, int head, int kb, char* kbuf, char* vbuf,
                                int wave) const {
     const int64_t first = ((sg.prefix_row0 + kb) * p.p_rs + (int64_t)head * p.p_hs) * 2;
-    const char* kbase = reinterpret_cast<const char*>(p.kp) + first;
-    const char* vbase = reinterpret_cast<const char*>(p.vp) + first;
+    const char* kbase = uniform_ptr(reinterpret_cast<const char*>(p.kp) + first);
+    const char* vbase = uniform_ptr(reinterpret_cast<const char*>(p.vp) + first);
 #pragma unroll
     for (int i = 0; i < T::kInstrPerWave; ++i) {
       const int instr = wave * T::kInstrPerWave + i;
@@ -203,6 +217,21 @@ __device__ inline uint64_t mask_bits(const uint32_t* row, int j0, int cnt) {
   return cnt >= 64 ? x : (x & ((1ull << cnt) - 1));
 }
 
+// Combine a value of lane l with that of lane l ^ 32 (the other half-wave),
+// with one v_permlane32_swap (a VALU op; no LDS round trip).
+__device__ inline float2 halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_halves(float v) {
+  const float2 h = halves(v);
+  return fmaxf(h.x, h.y);
+}
+__device__ inline float sum_halves(float v) {
+  const float2 h = halves(v);
+  return h.x + h.y;
+}
+
 constexpr float kRescaleSlack = 8.f;  // log2 units a stale running max may lag the true one
 constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" for the running max
 
@@ -211,7 +240,14 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   using T = Tile<D>;
   constexpr int KS = D / 16;  // k-steps of the QK^T product
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim
-  __shared__ __attribute__((aligned(1024))) char tiles[2][2][T::kBytes];  // [buffer][K, V]
+  // Double-buffered K and V tiles, four separate LDS objects: every access
+  // names its buffer statically (the tile loop is unrolled by two), so the
+  // compiler can tell that reading one buffer does not depend on the
+  // asynchronous global->LDS loads still filling the other.
+  __shared__ __attribute__((aligned(1024))) char k0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char k1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v1[T::kBytes];
   extern __shared__ uint32_t dyn[];  // [max_n] parents, then [mask_rows][mask_words] ancestor masks
 
   // ---- work item (XCD-aware remap: consecutive items share an XCD) ----
@@ -228,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int lr = lane & 31;   // query row within the wave
   const int hh = lane >> 5;   // half-wave
   const int g = p.g;
@@ -246,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   const int key_lo = split * p.chunk;
   int key_hi = min(key_lo + p.chunk, sg.P + sg.n);
   key_hi = min(key_hi, sg.P + node_hi + 1);  // later tree keys are no one's ancestor here
-  const int ntiles = key_hi > key_lo ? (key_hi - key_lo + kBN - 1) / kBN : 0;
+  const int ntiles = __builtin_amdgcn_readfirstlane(key_hi > key_lo ? (key_hi - key_lo + kBN - 1) / kBN : 0);
 
   // tiles below this key are wholly prefix and take the fast load path
   const int fast_end = min(sg.P, key_hi);
@@ -254,9 +290,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   pl.init(p.p_rs, wave, lane);
   if (ntiles > 0) {
     if (key_lo + kBN <= fast_end)
-      pl.issue(p, sg, head, key_lo, tiles[0][0], tiles[0][1], wave);
+      pl.issue(p, sg, head, key_lo, k0, v0, wave);
     else
-      issue_tile<D>(p, sg, head, key_lo, key_hi, tiles[0][0], tiles[0][1], wave, lane);
+      issue_tile<D>(p, sg, head, key_lo, key_hi, k0, v0, wave, lane);
   }
 
   uint32_t* par_s = dyn;
@@ -310,32 +346,64 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   const int v_chunk_lo = (grp & 1) * 2 + ((s16 & 3) >> 1);    // + 4db, then swizzled
   const int v_in = (s16 & 1) * 8;
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile: keys kb .. kb+63 from (kt, vt); the next tile is prefetched into (nk, nv).
+  auto step = [&](const int t, const char* kt, const char* vt, char* nk, char* nv) __attribute__((always_inline)) {
     const int kb = key_lo + t * kBN;
-    const int cur = t & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile t have landed (vmcnt = 0)
     __syncthreads();                     // everyone's have; everyone is done with tile t-1
     if (t + 1 < ntiles) {
       if (kb + 2 * kBN <= fast_end)
-        pl.issue(p, sg, head, kb + kBN, tiles[cur ^ 1][0], tiles[cur ^ 1][1], wave);
+        pl.issue(p, sg, head, kb + kBN, nk, nv, wave);
       else
-        issue_tile<D>(p, sg, head, kb + kBN, key_hi, tiles[cur ^ 1][0], tiles[cur ^ 1][1], wave, lane);
+        issue_tile<D>(p, sg, head, kb + kBN, key_hi, nk, nv, wave, lane);
     }
-    const char* kt = tiles[cur][0];
-    const char* vt = tiles[cur][1];
 
-    // S^T block bb (keys kb + 32bb ..): lane (lr, hh) gets keys 32bb + 8(j/4) + 4hh + (j%4), j = 0..15
-    f32x16 sc[2];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sc[bb][j] = 0.f;
+    // S^T block bb (keys kb + 32bb ..): lane (lr, hh) gets keys 32bb + 8(j/4) + 4hh + (j%4), j = 0..15.
+    // Operand reads are phased so that at most one K block and half of the V
+    // operands are in registers at a time (the kernel runs two waves per SIMD,
+    // 256 registers each); scheduling barriers keep the compiler from hoisting
+    // later reads into earlier phases.
+    auto load_k = [&](bf16x8* ka, int bb) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const int chunk = (2 * k + hh) ^ k_swz(lr);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + bb * 32 * T::kRowBytes + k_off + chunk * 16);
-        sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[k], sc[bb], 0, 0, 0);
+        const int chunk = (2 * k + hh) ^ k_swz<D>(lr);
+        ka[k] = *reinterpret_cast<const bf16x8*>(kt + bb * 32 * T::kRowBytes + k_off + chunk * 16);
       }
+    };
+    // V^T operand (i, bb, sub): d = 32i .., keys 32bb + 16sub ..
+    auto load_v = [&](bf16x8* va, int i0, int i1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = i0; i < i1; ++i) {
+        const int vch = ((i * 4 + v_chunk_lo) ^ v_swz<D>(v_row)) * 16 + v_in;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const char* vp0 = vt + (bb * 32 + sub * 16 + v_row) * T::kRowBytes + vch;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)vp0);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vp0 + 8 * T::kRowBytes));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            va[((i - i0) * 2 + bb) * 2 + sub] = *reinterpret_cast<const bf16x8*>(&a8);
+          }
+      }
+    };
+    constexpr int kVHalf = DB / 2 > 0 ? DB / 2 : 1;  // d-blocks whose V operands are read before the softmax
+    f32x16 sc[2];
+    bf16x8 va[kVHalf * 4];
+    {
+      bf16x8 ka[KS];
+      load_k(ka, 0);
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[0] : f32x16{}, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(ka, 1);
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[1] : f32x16{}, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(va, 0, kVHalf);
     }
 
     // ---- mask (tiles touching tree keys or the range end), then the running max ----
@@ -345,12 +413,15 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       if (npre > 0) vis = npre >= 64 ? ~0ull : ((1ull << npre) - 1);
       const int tlo = max(sg.P, kb), thi = min(key_hi, kb + kBN);
       if (row_ok && thi > tlo) vis |= mask_bits(my_mask, tlo - sg.P, thi - tlo) << (tlo - kb);
+      // this half-wave's keys sit at bits 32bb + 8(j/4) + 4hh + (j%4); after the
+      // per-lane shift by 4hh every bit position below is a constant
+      const uint64_t vh = vis >> (hh * 4);
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int kk = bb * 32 + (j >> 2) * 8 + hh * 4 + (j & 3);
-          if (!((vis >> kk) & 1ull)) sc[bb][j] = -INFINITY;
+          const int kk = bb * 32 + (j >> 2) * 8 + (j & 3);
+          if (!((vh >> kk) & 1ull)) sc[bb][j] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -358,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sc[bb][j], sc[bb][j + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const float mt = mx * c;
     // Rescale only when a row's max jumps by more than the slack (rare after
     // the first tiles). The decision is per row, so a row's arithmetic depends
@@ -390,27 +461,33 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);  // sums the rounded probabilities
       }
 
-    // ---- O^T += V^T P^T; V^T operands come from row-major V via transposing LDS reads ----
+    // ---- O^T += V^T P^T, first the d-blocks whose operands are in registers ----
 #pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      const int vch = ((i * 4 + v_chunk_lo) ^ (2 * (v_row & 3))) * 16 + v_in;
+    for (int i = 0; i < kVHalf; ++i)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const char* vp0 = vt + (bb * 32 + sub * 16 + v_row) * T::kRowBytes + vch;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)vp0);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vp0 + 8 * T::kRowBytes));
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&a8), pb[bb][sub],
-                                                             acc[i], 0, 0, 0);
-        }
+        for (int sub = 0; sub < 2; ++sub)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(i * 2 + bb) * 2 + sub], pb[bb][sub], acc[i], 0, 0, 0);
+    if constexpr (DB > kVHalf) {
+      load_v(va, kVHalf, DB);
+#pragma unroll
+      for (int i = kVHalf; i < DB; ++i)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[((i - kVHalf) * 2 + bb) * 2 + sub], pb[bb][sub],
+                                                               acc[i], 0, 0, 0);
     }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, k0, v0, k1, v1);
+    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
   }
 
   // ---- epilogue: lane (lr, hh) holds O^T[d][row lr] for d = 32i + 8(j/4) + 4hh + (j%4) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   if (sg.splits == 1) {
     const float inv = 1.f / l_tot;
@@ -437,11 +514,15 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   }
 }
 
-// Merge the per-chunk partials of split sequences: one wave per (node, query head).
+// Merge the per-chunk partials of split sequences. A thread owns four
+// consecutive dims of one (node, query head) row, so the threads of a row read
+// each chunk's partial as one contiguous 512-byte (d = 128) line.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int kTpr = D / 4;          // threads per row
+  constexpr int kRpb = 256 / kTpr;     // rows per block
+  const int row = blockIdx.x * kRpb + threadIdx.x / kTpr;
+  const int c4 = threadIdx.x % kTpr;
   if (row >= p.comb_rows) return;
   int s = -1;
   for (int i = 0; i < p.nseq; ++i)
@@ -451,33 +532,45 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   const int r = row - sg.comb_start;  // = node * Hq + qh
   if (r >= sg.n * p.Hq) return;
   const int node = r / p.Hq, qh = r % p.Hq;
-  float m = -INFINITY;
-  for (int k = 0; k < sg.splits; ++k) {
-    const int64_t prow = (int64_t)sg.part_base + ((int64_t)k * sg.n + node) * p.Hq + qh;
-    m = fmaxf(m, p.part_ml[prow].x);
-  }
-  constexpr int E = D / 64;  // elements per lane
-  float o[E];
+  // partial row of chunk k: part_base + (k * n + node) * Hq + qh = part_base + r + k * n * Hq
+  const int64_t prow0 = (int64_t)sg.part_base + r;
+  const int64_t kstride = (int64_t)sg.n * p.Hq;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o);
+  // One pass with a running maximum; chunks are loaded eight at a time so
+  // that their loads are in flight together.
+  constexpr int kBatch = 8;
+  float m = -INFINITY, l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < sg.splits; k0 += kBatch) {
+    float2 ml[kBatch];
+    float4 v[kBatch];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  float l = 0.f;
-  for (int k = 0; k < sg.splits; ++k) {
-    const int64_t prow = (int64_t)sg.part_base + ((int64_t)k * sg.n + node) * p.Hq + qh;
-    const float2 ml = p.part_ml[prow];
-    if (ml.y == 0.f) continue;  // chunk saw no visible key for this row
-    const float w = __builtin_amdgcn_exp2f(ml.x - m);
-    l += w * ml.y;
-    const float* po = p.part_o + prow * D + lane * E;
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = min(k0 + u, sg.splits - 1);
+      const int64_t prow = prow0 + k * kstride;
+      ml[u] = p.part_ml[prow];
+      v[u] = po[prow * kTpr + c4];
+    }
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += w * po[e];
+    for (int u = 0; u < kBatch; ++u) {
+      // a chunk that saw no visible key for this row (l = 0) contributes nothing
+      if (k0 + u < sg.splits && ml[u].y > 0.f) {
+        const float mn = fmaxf(m, ml[u].x);
+        const float a = __builtin_amdgcn_exp2f(m - mn);
+        const float w = __builtin_amdgcn_exp2f(ml[u].x - mn);
+        l = l * a + w * ml[u].y;
+        o.x = o.x * a + w * v[u].x;
+        o.y = o.y * a + w * v[u].y;
+        o.z = o.z * a + w * v[u].z;
+        o.w = o.w * a + w * v[u].w;
+        m = mn;
+      }
+    }
   }
   const float inv = 1.f / l;
-  bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    __bf16 v = (__bf16)(o[e] * inv);
-    orow[e] = *reinterpret_cast<bf16_bits*>(&v);
-  }
+  __bf16 o4[4] = {(__bf16)(o.x * inv), (__bf16)(o.y * inv), (__bf16)(o.z * inv), (__bf16)(o.w * inv)};
+  bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + c4 * 4;
+  *reinterpret_cast<uint2*>(orow) = *reinterpret_cast<uint2*>(o4);
 }
 
 // ---------------------------------------------------------------- host side
@@ -525,26 +618,24 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   const int g = d->num_q_heads / d->num_kv_heads;
   const int D = d->head_dim;
 
-  // Keys per split: automatic sizing aims for about 4 workgroups per CU in total.
+  // Keys per split. Every work item streams at most `chunk` keys; `chunk` is
+  // uniform, so items cost about the same and the per-XCD item ranges balance.
+  // It is sized so that the items fill the GPU's workgroup slots (two per CU)
+  // about once, with at least kMinTiles key tiles per item to amortise the
+  // prologue (Q rows, ancestor masks) and keep the tile pipeline busy.
   int64_t chunk = d->split_keys;
   if (chunk == 0) {
-    int64_t base_wg = 0, max_keys = 0, total_tiles = 0;
+    int64_t total_tiles = 0, max_keys = 0;
     for (int s = 0; s < d->num_seqs; ++s) {
       const int n = d->node_offsets[s + 1] - d->node_offsets[s];
-      const int64_t rt = ceil_div((int64_t)n * g, kBM) * d->num_kv_heads;
-      base_wg += rt;
       const int64_t keys = (int64_t)d->prefix_lens[s] + n;
+      const int64_t units = ceil_div((int64_t)n * g, kBM) * d->num_kv_heads;
+      total_tiles += units * ceil_div(keys, kBN);
       max_keys = std::max(max_keys, keys);
-      total_tiles += rt * ceil_div(keys, kBN);
     }
-    const int64_t target = 4LL * cus;
-    if (base_wg >= target) {
-      chunk = ceil_div(max_keys, kBN) * kBN;  // no split
-    } else {
-      // tiles per workgroup so that the total is ~target, at least 8 tiles (512 keys)
-      int64_t tiles = std::max<int64_t>(8, ceil_div(total_tiles, target));
-      chunk = tiles * kBN;
-    }
+    const int64_t slots = 2LL * cus;
+    const int64_t tiles = std::max<int64_t>(kMinTiles, ceil_div(total_tiles, slots));
+    chunk = std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
   }
   if (chunk > (int64_t)1 << 30) chunk = (int64_t)1 << 30;
 
@@ -590,7 +681,7 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
     a.comb_rows = comb;
     plan->launches.push_back(a);
     plan->grid.push_back(a.per_xcd * kXcds);
-    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 4) : 0);
+    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 4)) : 0);
     plan->lds.push_back(sizeof(uint32_t) * ((size_t)a.max_n + (size_t)a.mask_rows * a.mask_words));
   }
   (void)D;
