@@ -10,26 +10,34 @@
 //    packed with the tree's nodes into n*g query rows, so one KV head's keys
 //    meet a dense (n*g) x keys score block -- a real contraction for the
 //    matrix cores even though n is a few hundred at most.
-//  * A workgroup (4 waves) owns 128 query rows of one (sequence, KV head) and
-//    one chunk of that sequence's keys. Keys are visited in tiles of 64; each
-//    tile of K and V is staged in LDS once and read by all four waves. Two
-//    workgroups share a CU, so one's tile loads overlap the other's math.
-//  * Each wave holds 32 query rows. Scores are computed transposed,
-//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so that every lane ends up
-//    holding the scores of ONE query row: the softmax needs no cross-lane
-//    traffic except one exchange between the two half-waves, and the
-//    probabilities are already laid out as the B operand of O^T = V^T P^T.
-//    V is therefore staged transposed (V^T, d-major) in LDS.
-//  * Online softmax in the exp2 domain, fp32 statistics and accumulators;
-//    probabilities are rounded to bf16 (nearest-even) for the PV product.
+//  * A workgroup of eight waves (two per SIMD, one workgroup per CU); each
+//    wave owns 32 query rows. The workgroup is WM row groups x WN key slices
+//    (WM * WN = 8): 256 rows x 64 keys per step for large trees, 128 x 128 or
+//    64 x 256 for small ones. Every K/V tile staged in LDS serves all the
+//    workgroup's rows, and the key slices of one row group are merged through
+//    LDS at the end.
+//  * Scores are computed transposed, S^T = K Q^T, so every lane holds the
+//    scores of one query row: the softmax needs no cross-lane traffic except
+//    one v_permlane32_swap between half-waves, and the probabilities are
+//    already the B operand of O^T = V^T P^T. V stays row-major in LDS; its
+//    transposed operand comes from ds_read_b64_tr_b16.
+//  * K/V tiles go from global memory straight to LDS (global_load_lds_dwordx4)
+//    through a ring of up to four stages, so that up to three tiles are in
+//    flight while one is consumed: the load latency (one to three
+//    microseconds under load) times the bytes one step consumes is what the
+//    ring must cover. Each stage is its own LDS object so the compiler can see
+//    that reading one stage does not wait on the loads filling the others.
+//  * Online softmax in the exp2 domain with fp32 statistics and accumulators;
+//    the running max is rescaled lazily; probabilities are rounded to bf16
+//    (nearest-even) for the PV product and the row sums add those rounded
+//    values.
 //  * Prefix keys need no mask. For tree keys the ancestor bitmask of each of
-//    the workgroup's nodes is built in LDS by walking parent pointers.
-//    Because parent[i] < i, a node's ancestors never exceed it, so tree keys
-//    beyond the workgroup's last node are skipped outright.
-//  * Sequences with too few row tiles to fill the GPU split their keys into
-//    chunks; partial (O, m, l) go to a workspace and a second kernel merges
-//    them with log-sum-exp weights.
-//  * Work items are remapped so that the row tiles sharing one KV chunk are
+//    the workgroup's nodes is built in LDS by walking parent pointers; because
+//    parent[i] < i, tree keys beyond the workgroup's last node are skipped.
+//  * When there are too few (sequence, KV head, row tile) units to occupy the
+//    GPU, each unit's keys are split into chunks; partial (O, m, l) go to the
+//    workspace and a second kernel merges them with log-sum-exp weights.
+//  * Work items are ordered so that the row tiles sharing one key chunk are
 //    dispatched to the same XCD (workgroups go round-robin over the 8 XCDs),
 //    which keeps that chunk's K/V in one L2.
 
@@ -39,6 +47,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -47,16 +56,25 @@ namespace dt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t bf16_bits;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
-constexpr int kBM = 128;        // query rows per workgroup
-constexpr int kBN = 64;         // keys per tile
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kMaxSeqs = 32;    // sequences per launch (host loops over larger batches)
+constexpr int kWaveRows = 32;    // query rows per wave (one 32-row MFMA block)
+constexpr int kBN = 64;          // keys per wave per step
+constexpr int kWaves = 8;        // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSeqs = 32;     // sequences per launch (host loops over larger batches)
 constexpr int kXcds = 8;
-constexpr int kMinTiles = 4;   // key tiles per work item at least (automatic split sizing)
+constexpr int kStageBudget = 128 * 1024;  // LDS bytes for the K/V pipeline
+constexpr int kLdsBytes = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.f;  // log2 units a stale running max may lag the true one
+constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" for the running max
 
 struct SeqGeom {
   int64_t prefix_row0;  // first prefix row of this sequence
@@ -64,7 +82,7 @@ struct SeqGeom {
   int32_t n;            // nodes
   int32_t P;            // prefix length
   int32_t splits;       // key chunks
-  int32_t row_tiles;    // ceil(n*g / kBM)
+  int32_t row_tiles;    // ceil(n*g / rows per workgroup)
   int32_t item_start;   // first work item
   int32_t part_base;    // first partial row (split sequences), else -1
   int32_t comb_start;   // first combine row (split sequences)
@@ -101,71 +119,63 @@ __device__ inline int find_seq(const AttnParams& p, int item) {
   return s;
 }
 
-// 16-byte (8 x bf16) global load.
-__device__ inline uint4 ld16(const bf16_bits* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
-// LDS tiles (D = head dim, rows of D*2 bytes, no padding). A tile of 64 keys
-// of K and one of V per buffer, double-buffered. Rows are XOR-swizzled at
-// 16-byte-chunk granularity so that the MFMA operand reads are free of bank
-// conflicts while every lane's swizzle stays constant across the tile:
+// ---------------------------------------------------------------- tiles in LDS
+//
+// A tile is 64 keys x D dims of K or V, rows of 2D bytes without padding. The
+// rows are XOR-swizzled at 16-byte-chunk granularity:
 //   K: logical chunk c of row r sits at chunk c ^ k_swz(r)
 //   V: logical chunk c of row r sits at chunk c ^ v_swz(r)
-// Tiles are filled straight from global memory with global_load_lds_dwordx4
-// (each wave instruction writes 1 KB of consecutive LDS; the lane picks the
-// global chunk that belongs at its swizzled slot), so no registers stage them.
+// The LDS has 64 four-byte banks, i.e. a bank row of 256 bytes (one row of a
+// d = 128 tile, two rows of a d = 64 tile); the swizzles spread the 16 rows
+// read by one quarter-wave (K, 16-byte reads) and the 4 rows x 4 chunks read
+// by one half-wave (V, 8-byte transposing reads) over all 64 banks. Each
+// global_load_lds_dwordx4 instruction of a wave writes 1 KB of consecutive LDS;
+// every lane fetches the global chunk that belongs at its swizzled slot.
 template <int D>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
   static constexpr int kRowsPerInstr = 1024 / kRowBytes;  // rows one wave instruction fills
-  static constexpr int kInstrPerWave = kBN / kRowsPerInstr / 4;
-  static constexpr int kBytes = kBN * kRowBytes;          // one K (or V) tile
+  static constexpr int kBytes = kBN * kRowBytes;          // one 64-key tile
+  static constexpr int kSwzPeriod = D == 128 ? 4 : 2;     // instructions after which the lane swizzles repeat
 };
 
-// The LDS has 64 four-byte banks, i.e. a bank row of 256 bytes (one row of a
-// d = 128 tile, two rows of a d = 64 tile). The swizzles spread the 16 rows
-// read by one quarter-wave (K, 16-byte reads) and the 4 rows x 4 chunks read by
-// one half-wave (V, 8-byte transposing reads) over all 64 banks.
 template <int D>
 __device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
 __device__ inline int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+// Workgroup shape: WM row groups of 32 rows x WN key slices of 64 keys.
+template <int D, int WM>
+struct Shape {
+  static constexpr int WN = kWaves / WM;
+  static constexpr int RM = kWaveRows * WM;          // query rows per workgroup
+  static constexpr int KN = kBN * WN;                // keys per step
+  static constexpr int kPartBytes = KN * D * 2;      // the K (or V) part of a stage
+  static constexpr int kStageBytes = 2 * kPartBytes;
+  static constexpr int NST = kStageBudget / kStageBytes >= 4 ? 4 : (kStageBudget / kStageBytes >= 2 ? 2 : 1);
+  static constexpr int kInstr = kPartBytes / 1024 / kWaves;  // per wave, per tensor, per stage
+  static constexpr int kRegionBytes = 64 * (D / 32) * 16 * 4;  // one wave's accumulators
+  static constexpr int kMergeRegions = (WN - 1) * WM;           // key-slice merge buffer (stage 0's K and V parts)
+  static_assert(kInstr >= 1, "at least one load instruction per wave");
+  static_assert(kPartBytes % kRegionBytes == 0, "merge regions tile a stage part");
+  static_assert(kMergeRegions * kRegionBytes <= kStageBytes, "merge buffer fits in stage 0");
+};
 
-// Issue the loads of one K tile and one V tile (keys kb .. kb+63) into LDS,
-// general form: each row may come from the prefix cache or from the tree's own
-// K/V. Keys at or beyond key_end are read from row key_end-1 instead (always
-// valid; those keys are masked out, so their values only need to be finite).
-template <int D>
-__device__ inline void issue_tile(const AttnParams& p, const SeqGeom& sg, int head, int kb, int key_end,
-                                  char* kbuf, char* vbuf, int wave, int lane) {
-  using T = Tile<D>;
-  // The four base pointers as uniform values: selecting between them per lane
-  // must not turn into a per-lane load of the pointer (which would also wait
-  // for every load in flight).
-  const char* kp = reinterpret_cast<const char*>(p.kp);
-  const char* vp = reinterpret_cast<const char*>(p.vp);
-  const char* kt = reinterpret_cast<const char*>(p.kt);
-  const char* vt = reinterpret_cast<const char*>(p.vt);
-  const int rsub = lane / T::kChunks;  // row within the instruction's rows
-  const int pc = lane % T::kChunks;    // physical chunk this lane fills
-#pragma unroll
-  for (int i = 0; i < T::kInstrPerWave; ++i) {
-    const int instr = wave * T::kInstrPerWave + i;
-    const int row = instr * T::kRowsPerInstr + rsub;
-    int key = kb + row;
-    key = key < key_end ? key : key_end - 1;
-    const bool pre = key < sg.P;
-    const int64_t off = pre ? ((sg.prefix_row0 + key) * p.p_rs + (int64_t)head * p.p_hs) * 2
-                            : ((int64_t)(sg.node_off + key - sg.P) * p.t_rs + (int64_t)head * D) * 2;
-    const char* ksrc = (pre ? kp : kt) + off + ((pc ^ k_swz<D>(row)) << 4);
-    const char* vsrc = (pre ? vp : vt) + off + ((pc ^ v_swz<D>(row)) << 4);
-    __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_ptr)(kbuf + instr * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_ptr)(vbuf + instr * 1024), 16, 0, 0);
-  }
+// Workgroup barrier for the K/V pipeline: this wave's LDS reads are complete
+// (lgkmcnt = 0) and every wave has arrived. Unlike __syncthreads() it does not
+// wait for this wave's outstanding global->LDS loads, which belong to later
+// stages (each wave waits for the loads of the stage it is about to read
+// before arriving); the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ inline void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // A wave-uniform pointer, kept in scalar registers.
@@ -175,39 +185,6 @@ __device__ inline const char* uniform_ptr(const char* ptr) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
-
-// Fast form for tiles that lie wholly inside the prefix: one wave-uniform base
-// address per tile plus per-lane 32-bit byte offsets fixed for the whole loop.
-template <int D>
-struct PrefixLoads {
-  using T = Tile<D>;
-  uint32_t koff[T::kInstrPerWave];
-  uint32_t voff[T::kInstrPerWave];
-
-  __device__ inline void init(int64_t row_stride, int wave, int lane) {
-    const int rsub = lane / T::kChunks, pc = lane % T::kChunks;
-#pragma unroll
-    for (int i = 0; i < T::kInstrPerWave; ++i) {
-      const int row = (wave * T::kInstrPerWave + i) * T::kRowsPerInstr + rsub;
-      const uint32_t roff = (uint32_t)(row * row_stride * 2);
-      koff[i] = roff + ((pc ^ k_swz<D>(row)) << 4);
-      voff[i] = roff + ((pc ^ v_swz<D>(row)) << 4);
-    }
-  }
-
-  __device__ inline void issue(const AttnParams& p, const SeqGeom& sg, int head, int kb, char* kbuf, char* vbuf,
-                               int wave) const {
-    const int64_t first = ((sg.prefix_row0 + kb) * p.p_rs + (int64_t)head * p.p_hs) * 2;
-    const char* kbase = uniform_ptr(reinterpret_cast<const char*>(p.kp) + first);
-    const char* vbase = uniform_ptr(reinterpret_cast<const char*>(p.vp) + first);
-#pragma unroll
-    for (int i = 0; i < T::kInstrPerWave; ++i) {
-      const int instr = wave * T::kInstrPerWave + i;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + koff[i]), (lds_void_ptr)(kbuf + instr * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + voff[i]), (lds_void_ptr)(vbuf + instr * 1024), 16, 0, 0);
-    }
-  }
-};
 
 // Bits [j0, j0 + cnt) of an ancestor-mask row, cnt <= 64, j0 >= 0.
 __device__ inline uint64_t mask_bits(const uint32_t* row, int j0, int cnt) {
@@ -232,23 +209,29 @@ __device__ inline float sum_halves(float v) {
   return h.x + h.y;
 }
 
-constexpr float kRescaleSlack = 8.f;  // log2 units a stale running max may lag the true one
-constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" for the running max
-
-template <int D>
+template <int D, int WM>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p) {
   using T = Tile<D>;
+  using SH = Shape<D, WM>;
+  constexpr int WN = SH::WN, RM = SH::RM, KN = SH::KN, NST = SH::NST;
   constexpr int KS = D / 16;  // k-steps of the QK^T product
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim
-  // Double-buffered K and V tiles, four separate LDS objects: every access
-  // names its buffer statically (the tile loop is unrolled by two), so the
-  // compiler can tell that reading one buffer does not depend on the
-  // asynchronous global->LDS loads still filling the other.
-  __shared__ __attribute__((aligned(1024))) char k0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char v0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char k1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char v1[T::kBytes];
-  extern __shared__ uint32_t dyn[];  // [max_n] parents, then [mask_rows][mask_words] ancestor masks
+  constexpr int kPer = 2 * SH::kInstr;  // vector-memory operations per wave per stage
+
+  // K/V pipeline stages; the K and V tiles of every stage are separate LDS objects.
+  __shared__ __attribute__((aligned(1024))) char k0[SH::kPartBytes];
+  __shared__ __attribute__((aligned(1024))) char v0[SH::kPartBytes];
+  __shared__ __attribute__((aligned(1024))) char k1[NST > 1 ? SH::kPartBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) char v1[NST > 1 ? SH::kPartBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) char k2[NST > 2 ? SH::kPartBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) char v2[NST > 2 ? SH::kPartBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) char k3[NST > 3 ? SH::kPartBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) char v3[NST > 3 ? SH::kPartBytes : 1024];
+  struct Stage {
+    char* k;
+    char* v;
+  };
+  extern __shared__ uint32_t dyn[];  // parents, ancestor masks, key-slice merge statistics
 
   // ---- work item (XCD-aware remap: consecutive items share an XCD) ----
   const int b = blockIdx.x;
@@ -265,38 +248,43 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
-  const int lr = lane & 31;   // query row within the wave
-  const int hh = lane >> 5;   // half-wave
+  const int wm = wave % WM;  // row group
+  const int wn = wave / WM;  // key slice
+  const int lr = lane & 31;  // query row within a 32-row block
+  const int hh = lane >> 5;  // half-wave
   const int g = p.g;
   const int nrows = sg.n * g;
 
-  const int row0 = tile * kBM;
-  const int my_row = row0 + wave * 32 + lr;
+  const int row0 = tile * RM;
+  const int my_row = row0 + wm * kWaveRows + lr;
   const bool row_ok = my_row < nrows;
   const int my_node = row_ok ? my_row / g : 0;
   const int my_qh = head * g + (row_ok ? my_row % g : 0);
   const int node_lo = row0 / g;
-  const int node_hi = min(sg.n - 1, (min(row0 + kBM, nrows) - 1) / g);
+  const int node_hi = min(sg.n - 1, (min(row0 + RM, nrows) - 1) / g);
 
   // ---- key range of this work item ----
   const int key_lo = split * p.chunk;
   int key_hi = min(key_lo + p.chunk, sg.P + sg.n);
   key_hi = min(key_hi, sg.P + node_hi + 1);  // later tree keys are no one's ancestor here
-  const int ntiles = __builtin_amdgcn_readfirstlane(key_hi > key_lo ? (key_hi - key_lo + kBN - 1) / kBN : 0);
-
-  // tiles below this key are wholly prefix and take the fast load path
-  const int fast_end = min(sg.P, key_hi);
-  PrefixLoads<D> pl;
-  pl.init(p.p_rs, wave, lane);
-  if (ntiles > 0) {
-    if (key_lo + kBN <= fast_end)
-      pl.issue(p, sg, head, key_lo, k0, v0, wave);
-    else
-      issue_tile<D>(p, sg, head, key_lo, key_hi, k0, v0, wave, lane);
-  }
+  const int nsteps = __builtin_amdgcn_readfirstlane(key_hi > key_lo ? (key_hi - key_lo + KN - 1) / KN : 0);
+  const int fast_end = min(sg.P, key_hi);    // keys below this are prefix keys
+  const int prefix_end = fast_end;           // ... and visible to every row
 
   uint32_t* par_s = dyn;
   uint32_t* masks = dyn + p.max_n;
+  float* merge_ml = reinterpret_cast<float*>(masks + p.mask_rows * p.mask_words);
+
+  // ---- Q rows (B operand of S^T = K Q^T): lane holds row lr, dims 16k + 8hh .. +7 ----
+  bf16x8 qreg[KS];
+  {
+    const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + k * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+      qreg[k] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
 
   // ---- ancestor bitmasks of this tile's nodes (only if tree keys are visited) ----
   if (key_hi > sg.P) {
@@ -304,9 +292,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     const int nmask = (node_hi - node_lo + 1) * p.mask_words;
     for (int i = tid; i < nmask; i += kThreads) masks[i] = 0u;
     __syncthreads();
-    if (tid <= node_hi - node_lo) {
-      uint32_t* row = masks + tid * p.mask_words;
-      int j = node_lo + tid;
+    for (int t = tid; t <= node_hi - node_lo; t += kThreads) {
+      uint32_t* row = masks + t * p.mask_words;
+      int j = node_lo + t;
       // Walk to the root; parent[j] < j bounds the walk even for a malformed array.
       for (;;) {
         row[j >> 5] |= 1u << (j & 31);
@@ -315,19 +303,62 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         j = pj;
       }
     }
+    __syncthreads();
   }
 
-  // ---- Q rows as the B operand of S^T = K Q^T: lane holds row lr, dims 16k + 8hh .. +7 ----
-  bf16x8 qreg[KS];
-  {
-    const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
+  // ---- K/V stage loads ----
+  const char* kp_base = reinterpret_cast<const char*>(p.kp);
+  const char* vp_base = reinterpret_cast<const char*>(p.vp);
+  const char* kt_base = reinterpret_cast<const char*>(p.kt);
+  const char* vt_base = reinterpret_cast<const char*>(p.vt);
+  const int rsub = lane / T::kChunks;  // row within an instruction's rows
+  const int pc = lane % T::kChunks;    // physical chunk this lane fills
+  // Per-lane byte offsets of the prefix fast path, one per load instruction of this wave.
+  uint32_t lane_k[SH::kInstr], lane_v[SH::kInstr];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      uint4 v = row_ok ? ld16(qrow + k * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
-      qreg[k] = *reinterpret_cast<bf16x8*>(&v);
-    }
+  for (int i = 0; i < SH::kInstr; ++i) {
+    const int row = (wave * SH::kInstr + i) * T::kRowsPerInstr + rsub;
+    lane_k[i] = (uint32_t)(rsub * p.p_rs * 2) + ((pc ^ k_swz<D>(row)) << 4);
+    lane_v[i] = (uint32_t)(rsub * p.p_rs * 2) + ((pc ^ v_swz<D>(row)) << 4);
   }
+  // Issue the loads of the stage that holds keys kb .. kb + KN - 1.
+  auto issue = [&](int kb, Stage stage) __attribute__((always_inline)) {
+    if (kb + KN <= fast_end) {
+      // wholly inside the prefix: uniform base per instruction plus the lane offsets
+      // (uniform 64-bit base in scalar registers + a 32-bit lane offset)
+      const int64_t first = ((sg.prefix_row0 + kb) * p.p_rs + (int64_t)head * p.p_hs) * 2;
+#pragma unroll
+      for (int i = 0; i < SH::kInstr; ++i) {
+        const int instr = wave * SH::kInstr + i;
+        const int64_t roff = first + (int64_t)instr * T::kRowsPerInstr * p.p_rs * 2;
+        const char* kb_i = uniform_ptr(kp_base + roff);
+        const char* vb_i = uniform_ptr(vp_base + roff);
+        __builtin_amdgcn_global_load_lds((const void*)(kb_i + lane_k[i]), (lds_void_ptr)(stage.k + instr * 1024), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb_i + lane_v[i]), (lds_void_ptr)(stage.v + instr * 1024), 16,
+                                         0, 0);
+      }
+    } else {
+      // general form: rows from the prefix cache or from the tree's own K/V;
+      // keys at or beyond key_hi re-read row key_hi - 1 (finite; masked out)
+#pragma unroll
+      for (int i = 0; i < SH::kInstr; ++i) {
+        const int instr = wave * SH::kInstr + i;
+        const int row = instr * T::kRowsPerInstr + rsub;
+        int key = kb + row;
+        key = key < key_hi ? key : key_hi - 1;
+        const bool pre = key < sg.P;
+        const int64_t off = pre ? ((sg.prefix_row0 + key) * p.p_rs + (int64_t)head * p.p_hs) * 2
+                                : ((int64_t)(sg.node_off + key - sg.P) * p.t_rs + (int64_t)head * D) * 2;
+        const char* ksrc = (pre ? kp_base : kt_base) + off + ((pc ^ k_swz<D>(row)) << 4);
+        const char* vsrc = (pre ? vp_base : vt_base) + off + ((pc ^ v_swz<D>(row)) << 4);
+        __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_ptr)(stage.k + instr * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_ptr)(stage.v + instr * 1024), 16, 0, 0);
+      }
+    }
+  };
 
+  // ---- running state ----
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i)
@@ -336,83 +367,107 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   float m_run = kInitMax;  // running max (log2 units; may lag the true max by < kRescaleSlack)
   float l_run = 0.f;       // running sum over this half-wave's keys
   const float c = p.scale_log2;
-  const int prefix_end = min(sg.P, key_hi);  // keys below this are visible to every row
   const uint32_t* my_mask = masks + (my_node - node_lo) * p.mask_words;
 
-  // per-lane LDS byte offsets of the operand reads
-  const int k_off = lr * T::kRowBytes;                       // + chunk, see below
+  // per-lane LDS byte offsets of the operand reads (within the wave's 64-key slice)
+  const int k_off = lr * T::kRowBytes;
   const int s16 = lane & 15, grp = lane >> 4;
-  const int v_row = hh * 4 + (s16 >> 2);                     // + 32bb + 16sub + 8hi
-  const int v_chunk_lo = (grp & 1) * 2 + ((s16 & 3) >> 1);    // + 4db, then swizzled
+  const int v_row = hh * 4 + (s16 >> 2);                    // + 32bb + 16sub + 8hi
+  const int v_chunk_lo = (grp & 1) * 2 + ((s16 & 3) >> 1);  // + 4i, then swizzled
   const int v_in = (s16 & 1) * 8;
 
-  // One tile: keys kb .. kb+63 from (kt, vt); the next tile is prefetched into (nk, nv).
-  auto step = [&](const int t, const char* kt, const char* vt, char* nk, char* nv) __attribute__((always_inline)) {
-    const int kb = key_lo + t * kBN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile t have landed (vmcnt = 0)
-    __syncthreads();                     // everyone's have; everyone is done with tile t-1
-    if (t + 1 < ntiles) {
-      if (kb + 2 * kBN <= fast_end)
-        pl.issue(p, sg, head, kb + kBN, nk, nv, wave);
-      else
-        issue_tile<D>(p, sg, head, kb + kBN, key_hi, nk, nv, wave, lane);
-    }
+  // Per-step pieces. S(step) = K Q^T of this wave's 64 keys of the step
+  // (registers sc), P(step) = its probabilities (registers pb, after the online
+  // softmax), and O^T += V^T P^T with the same step's V.
+  f32x16 sc[2];     // S^T blocks bb: lane (lr, hh) holds keys 32bb + 8(j/4) + 4hh + (j%4), j = 0..15
+  bf16x8 pb[2][2];  // P^T: B operand of the PV product, [bb][sub]
 
-    // S^T block bb (keys kb + 32bb ..): lane (lr, hh) gets keys 32bb + 8(j/4) + 4hh + (j%4), j = 0..15.
-    // Operand reads are phased so that at most one K block and half of the V
-    // operands are in registers at a time (the kernel runs two waves per SIMD,
-    // 256 registers each); scheduling barriers keep the compiler from hoisting
-    // later reads into earlier phases.
-    auto load_k = [&](bf16x8* ka, int bb) __attribute__((always_inline)) {
+  auto load_k = [&](const char* kt, bf16x8* ka, int bb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const int chunk = (2 * k + hh) ^ k_swz<D>(lr);
-        ka[k] = *reinterpret_cast<const bf16x8*>(kt + bb * 32 * T::kRowBytes + k_off + chunk * 16);
-      }
-    };
-    // V^T operand (i, bb, sub): d = 32i .., keys 32bb + 16sub ..
-    auto load_v = [&](bf16x8* va, int i0, int i1) __attribute__((always_inline)) {
+    for (int k = 0; k < KS; ++k) {
+      const int chunk = (2 * k + hh) ^ k_swz<D>(lr);
+      ka[k] = *reinterpret_cast<const bf16x8*>(kt + bb * 32 * T::kRowBytes + k_off + chunk * 16);
+    }
+  };
+  // V^T operands of d-blocks i0 .. i0+1, (i, bb, sub): d = 32i .., keys 32bb + 16sub ..
+  // The transposing reads are issued from inline assembly and completed by
+  // vt_wait(): every one of them reads a stage whose global->LDS loads this
+  // wave has already waited for (the compiler cannot see that and would
+  // otherwise wait for all loads in flight, stalling the prefetch ring).
+  auto load_v = [&](const char* vt, uint2* vr, int i0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = i0; i < i1; ++i) {
-        const int vch = ((i * 4 + v_chunk_lo) ^ v_swz<D>(v_row)) * 16 + v_in;
+    for (int i = i0; i < i0 + 2; ++i) {
+      const int vch = ((i * 4 + v_chunk_lo) ^ v_swz<D>(v_row)) * 16 + v_in;
+      const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(vt + v_row * T::kRowBytes + vch);
+      uint2* r = vr + (i - i0) * 8;  // [bb][sub][lo, hi]
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
+          "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+          "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
+          "ds_read_b64_tr_b16 %7, %8 offset:%16"
+          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+          : "v"(a), "i"(0 * T::kRowBytes), "i"(8 * T::kRowBytes), "i"(16 * T::kRowBytes), "i"(24 * T::kRowBytes),
+            "i"(32 * T::kRowBytes), "i"(40 * T::kRowBytes), "i"(48 * T::kRowBytes), "i"(56 * T::kRowBytes));
+    }
+  };
+  // Wait for this wave's outstanding LDS reads; the values pass through the
+  // statement so that nothing reads them earlier.
+  auto vt_wait = [&](uint2* vr) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
+                   "+v"(vr[7]), "+v"(vr[8]), "+v"(vr[9]), "+v"(vr[10]), "+v"(vr[11]), "+v"(vr[12]), "+v"(vr[13]),
+                   "+v"(vr[14]), "+v"(vr[15]));
+  };
+  // operand (il, bb, sub) of the d-block pair held in vr
+  auto v_operand = [&](const uint2* vr, int il, int bb, int sub) __attribute__((always_inline)) -> bf16x8 {
+    const uint2 lo = vr[il * 8 + (bb * 2 + sub) * 2], hi = vr[il * 8 + (bb * 2 + sub) * 2 + 1];
+    const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    return *reinterpret_cast<const bf16x8*>(&q);
+  };
+  static_assert(DB % 2 == 0, "d-blocks come in pairs");
+
+  // S(step): both 32-key blocks; one K block in registers at a time.
+  auto s_product = [&](const char* kt) __attribute__((always_inline)) {
+    bf16x8 ka[KS];
+    load_k(kt, ka, 0);
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[0] : f32x16{}, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kt, ka, 1);
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[1] : f32x16{}, 0, 0, 0);
+  };
+  // O^T += V^T P^T, two d-blocks at a time
+  auto pv_product = [&](const char* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i0 = 0; i0 < DB; i0 += 2) {
+      uint2 vr[16];
+      load_v(vt, vr, i0);
+      vt_wait(vr);
+#pragma unroll
+      for (int il = 0; il < 2; ++il)
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const char* vp0 = vt + (bb * 32 + sub * 16 + v_row) * T::kRowBytes + vch;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)vp0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vp0 + 8 * T::kRowBytes));
-            typedef short s16x8 __attribute__((ext_vector_type(8)));
-            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            va[((i - i0) * 2 + bb) * 2 + sub] = *reinterpret_cast<const bf16x8*>(&a8);
-          }
-      }
-    };
-    constexpr int kVHalf = DB / 2 > 0 ? DB / 2 : 1;  // d-blocks whose V operands are read before the softmax
-    f32x16 sc[2];
-    bf16x8 va[kVHalf * 4];
-    {
-      bf16x8 ka[KS];
-      load_k(ka, 0);
-#pragma unroll
-      for (int k = 0; k < KS; ++k)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[0] : f32x16{}, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_k(ka, 1);
-#pragma unroll
-      for (int k = 0; k < KS; ++k)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[1] : f32x16{}, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(va, 0, kVHalf);
+          for (int sub = 0; sub < 2; ++sub)
+            acc[i0 + il] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(vr, il, bb, sub), pb[bb][sub],
+                                                                   acc[i0 + il], 0, 0, 0);
     }
-
-    // ---- mask (tiles touching tree keys or the range end), then the running max ----
-    if (kb + kBN > prefix_end) {
-      uint64_t vis = 0;
-      const int npre = prefix_end - kb;
-      if (npre > 0) vis = npre >= 64 ? ~0ull : ((1ull << npre) - 1);
-      const int tlo = max(sg.P, kb), thi = min(key_hi, kb + kBN);
-      if (row_ok && thi > tlo) vis |= mask_bits(my_mask, tlo - sg.P, thi - tlo) << (tlo - kb);
+  };
+  // Mask and online softmax of S(step) into P(step).
+  auto softmax = [&](int step) __attribute__((always_inline)) {
+    const int kbw = key_lo + step * KN + wn * kBN;
+    if (kbw + kBN > prefix_end) {
+      const int npre = prefix_end - kbw;
+      uint64_t vis = npre <= 0 ? 0ull : (npre >= 64 ? ~0ull : ((1ull << npre) - 1));
+      const int tlo = max(sg.P, kbw), thi = min(key_hi, kbw + kBN);
+      if (row_ok && thi > tlo) vis |= mask_bits(my_mask, tlo - sg.P, thi - tlo) << (tlo - kbw);
       // this half-wave's keys sit at bits 32bb + 8(j/4) + 4hh + (j%4); after the
       // per-lane shift by 4hh every bit position below is a constant
       const uint64_t vh = vis >> (hh * 4);
@@ -432,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     mx = max_halves(mx);
     const float mt = mx * c;
     // Rescale only when a row's max jumps by more than the slack (rare after
-    // the first tiles). The decision is per row, so a row's arithmetic depends
+    // the first steps). The decision is per row, so a row's arithmetic depends
     // on its own visible keys only; the branch is taken if any row needs it.
     const bool need = mt > m_run + kRescaleSlack;
     if (__any(need)) {
@@ -446,8 +501,6 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
     }
     const float neg_m = -m_run;
-    bf16x8 pb[2][2];
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -460,35 +513,171 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         pb[bb][j >> 3][(j & 7) + 1] = pr[1];
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);  // sums the rounded probabilities
       }
+  };
+  // The whole step for one wave (the schedule without ping-pong).
+  auto compute = [&](int step, Stage stage) __attribute__((always_inline)) {
+    s_product(stage.k + wn * T::kBytes);
+    softmax(step);
+    pv_product(stage.v + wn * T::kBytes);
+  };
 
-    // ---- O^T += V^T P^T, first the d-blocks whose operands are in registers ----
-#pragma unroll
-    for (int i = 0; i < kVHalf; ++i)
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(i * 2 + bb) * 2 + sub], pb[bb][sub], acc[i], 0, 0, 0);
-    if constexpr (DB > kVHalf) {
-      load_v(va, kVHalf, DB);
-#pragma unroll
-      for (int i = kVHalf; i < DB; ++i)
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[((i - kVHalf) * 2 + bb) * 2 + sub], pb[bb][sub],
-                                                               acc[i], 0, 0, 0);
+  // ---- the pipeline: stage u of every group of NST steps lives in st<u> ----
+  auto stage_ptr = [&](auto U) __attribute__((always_inline)) -> Stage {
+    constexpr int u = decltype(U)::value;
+    if constexpr (u == 0) return Stage{k0, v0};
+    else if constexpr (u == 1) return Stage{k1, v1};
+    else if constexpr (u == 2) return Stage{k2, v2};
+    else return Stage{k3, v3};
+  };
+  // Wait until this wave's loads for `step` have landed: the loads of the
+  // later steps already issued may stay in flight.
+  auto wait_step = [&](int step) __attribute__((always_inline)) {
+    const int later = min(NST - 2, nsteps - 1 - step);
+    if (NST >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+    else if (NST >= 3 && later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  auto run_step = [&](int step, auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    wait_step(step);
+    stage_barrier();  // every wave's loads of this step have landed; everyone is done with step - 1
+    if constexpr (NST > 1) {
+      if (step + NST - 1 < nsteps)
+        issue(key_lo + (step + NST - 1) * KN, stage_ptr(std::integral_constant<int, (u + NST - 1) % NST>{}));
+    }
+    compute(step, stage_ptr(U));
+    if constexpr (NST == 1) {
+      stage_barrier();  // everyone is done with the only stage
+      if (step + 1 < nsteps) issue(key_lo + (step + 1) * KN, Stage{k0, v0});
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, k0, v0, k1, v1);
-    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+
+  if constexpr (NST == 4 && WN == 1) {
+    // Ping-pong: waves 0-3 (group A, one per SIMD) and waves 4-7 (group B) take
+    // turns. Every step has two phases, each closed by a workgroup barrier; in
+    // one a group runs its MFMA block -- O += V P of the previous step, then S
+    // of this one -- while the other group runs the softmax of its step, so each
+    // SIMD's matrix core is fed by one of its two waves while the other works
+    // on the VALU. Group B trails group A by one phase. Tile s is read from
+    // phase 2s (A's S) to phase 2s + 3 (B's PV); its stage is refilled with
+    // tile s + 4 at phase 2s + 4, and each tile is loaded two steps ahead.
+    const bool grp_b = wave >= 4;
+    auto x_block = [&](int s, Stage cur, Stage prev) __attribute__((always_inline)) {
+      if (s > 0) pv_product(prev.v);
+      s_product(cur.k);
+    };
+    // even phase of step s: tile s must have landed (tile s + 1 may still be
+    // in flight); after the barrier, tile s + 2 is requested
+    auto even_barrier = [&](int s, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      stage_barrier();
+      if (s + 2 < nsteps) issue(key_lo + (s + 2) * KN, stage_ptr(std::integral_constant<int, (u + 2) % 4>{}));
+    };
+    // The two groups run separate copies of the loop (so that S and P are
+    // never both live across a barrier) with the same sequence of barriers.
+    auto group_a = [&](int s, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      even_barrier(s, U);
+      x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
+      stage_barrier();
+      softmax(s);
+    };
+    auto group_b = [&](int s, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      even_barrier(s, U);
+      if (s > 0) softmax(s - 1);
+      stage_barrier();
+      x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
+    };
+    if (nsteps > 0) issue(key_lo, Stage{k0, v0});
+    if (nsteps > 1) issue(key_lo + KN, Stage{k1, v1});
+    if (!grp_b) {
+      for (int s0 = 0; s0 < nsteps; s0 += 4) {
+        group_a(s0, std::integral_constant<int, 0>{});
+        if (s0 + 1 < nsteps) group_a(s0 + 1, std::integral_constant<int, 1>{});
+        if (s0 + 2 < nsteps) group_a(s0 + 2, std::integral_constant<int, 2>{});
+        if (s0 + 3 < nsteps) group_a(s0 + 3, std::integral_constant<int, 3>{});
+      }
+    } else {
+      for (int s0 = 0; s0 < nsteps; s0 += 4) {
+        group_b(s0, std::integral_constant<int, 0>{});
+        if (s0 + 1 < nsteps) group_b(s0 + 1, std::integral_constant<int, 1>{});
+        if (s0 + 2 < nsteps) group_b(s0 + 2, std::integral_constant<int, 2>{});
+        if (s0 + 3 < nsteps) group_b(s0 + 3, std::integral_constant<int, 3>{});
+      }
+    }
+    // drain: A finishes the last PV; B its last softmax, then its last PV
+    if (nsteps > 0) {
+      const int last = nsteps - 1;
+      const Stage tail = (last & 3) == 0 ? Stage{k0, v0} : (last & 3) == 1 ? Stage{k1, v1}
+                       : (last & 3) == 2 ? Stage{k2, v2} : Stage{k3, v3};
+      stage_barrier();
+      if (!grp_b) pv_product(tail.v);
+      else softmax(last);
+      stage_barrier();
+      if (grp_b) pv_product(tail.v);
+    }
+  } else {
+  // prologue: the first NST - 1 stages (one if NST == 1)
+  if (nsteps > 0) issue(key_lo, Stage{k0, v0});
+  if constexpr (NST > 2) {
+    if (nsteps > 1) issue(key_lo + KN, Stage{k1, v1});
+    if (nsteps > 2) issue(key_lo + 2 * KN, Stage{k2, v2});
+  }
+  for (int s0 = 0; s0 < nsteps; s0 += NST) {
+    run_step(s0, std::integral_constant<int, 0>{});
+    if constexpr (NST > 1) if (s0 + 1 < nsteps) run_step(s0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST > 2) if (s0 + 2 < nsteps) run_step(s0 + 2, std::integral_constant<int, 2>{});
+    if constexpr (NST > 3) if (s0 + 3 < nsteps) run_step(s0 + 3, std::integral_constant<int, 3>{});
+  }
   }
 
   // ---- epilogue: lane (lr, hh) holds O^T[d][row lr] for d = 32i + 8(j/4) + 4hh + (j%4) ----
-  const float l_tot = sum_halves(l_run);
-  if (!row_ok) return;
+  float l_tot = sum_halves(l_run);
+
+  if constexpr (WN > 1) {
+    // merge the key slices of each row group through LDS (stage 0 is free now)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    // region r (one wave's accumulators) lives in k0, then continues in v0
+    auto region = [&](int r) __attribute__((always_inline)) -> float* {
+      constexpr int kPerPart = SH::kPartBytes / SH::kRegionBytes;
+      return reinterpret_cast<float*>(r < kPerPart ? k0 + r * SH::kRegionBytes : v0 + (r - kPerPart) * SH::kRegionBytes);
+    };
+    if (wn > 0) {
+      const int r = (wn - 1) * WM + wm;
+      float* dst = region(r);
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[(i * 16 + j) * 64 + lane] = acc[i][j];
+      float* ml = merge_ml + (r * 64 + lane) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+    __syncthreads();
+    if (wn == 0) {
+      for (int w2 = 1; w2 < WN; ++w2) {
+        const int r = (w2 - 1) * WM + wm;
+        const float* src = region(r);
+        const float* ml = merge_ml + (r * 64 + lane) * 2;
+        const float m2 = ml[0], l2 = ml[1];
+        const float mn = fmaxf(m_run, m2);
+        const float a1 = __builtin_amdgcn_exp2f(m_run - mn);
+        const float a2 = __builtin_amdgcn_exp2f(m2 - mn);
+        m_run = mn;
+        l_tot = l_tot * a1 + l2 * a2;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] * a1 + src[(i * 16 + j) * 64 + lane] * a2;
+      }
+    }
+  }
+  if (wn != 0 || !row_ok) return;
+
   if (sg.splits == 1) {
     const float inv = 1.f / l_tot;
     bf16_bits* orow = p.out + (int64_t)(sg.node_off + my_node) * p.out_rs + (int64_t)my_qh * D;
@@ -516,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 
 // Merge the per-chunk partials of split sequences. A thread owns four
 // consecutive dims of one (node, query head) row, so the threads of a row read
-// each chunk's partial as one contiguous 512-byte (d = 128) line.
+// each chunk's partial as one contiguous line.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   constexpr int kTpr = D / 4;          // threads per row
@@ -576,6 +765,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
 // ---------------------------------------------------------------- host side
 
 struct Plan {
+  int wm = 8;                        // row groups per workgroup (64, 128 or 256 rows)
   std::vector<AttnParams> launches;  // one per group of <= kMaxSeqs sequences
   std::vector<int> grid;             // workgroups per launch
   std::vector<int> comb_grid;        // combine blocks per launch (0 = none)
@@ -604,9 +794,69 @@ int check_desc(const dt_attn_desc* d) {
   if (qrs < d->num_q_heads * D || ors < d->num_q_heads * D || trs < d->num_kv_heads * D) return DT_ERR_SHAPE;
   if (qrs % 8 || ors % 8 || trs % 8 || d->prefix_row_stride % 8 || d->prefix_head_stride % 8) return DT_ERR_SHAPE;
   if (d->prefix_row_stride < 0 || d->prefix_head_stride < 0) return DT_ERR_SHAPE;
-  // the kernel addresses 64 cache rows of a tile with 32-bit byte offsets
+  // per-lane offsets within one load instruction's rows are 32-bit
   if (d->prefix_row_stride >= ((int64_t)1 << 24)) return DT_ERR_UNSUPPORTED;
   return DT_OK;
+}
+
+template <int D, int WM>
+size_t static_lds() {
+  using SH = Shape<D, WM>;
+  return (size_t)SH::kStageBytes * SH::NST + 1024 * (4 - SH::NST);
+}
+
+size_t static_lds_for(int D, int wm) {
+  if (D == 128) return wm == 8 ? static_lds<128, 8>() : wm == 4 ? static_lds<128, 4>() : static_lds<128, 2>();
+  return wm == 8 ? static_lds<64, 8>() : wm == 4 ? static_lds<64, 4>() : static_lds<64, 2>();
+}
+
+// Dynamic LDS of one launch: parents, ancestor masks and the key-slice merge statistics.
+size_t dynamic_lds(int max_n, int g, int wm) {
+  const int rm = kWaveRows * wm;
+  const size_t mask_rows = (size_t)((rm - 1) / g + 2);
+  const size_t mask_words = (size_t)((max_n + 31) / 32 + 2);
+  const size_t merge = (size_t)(kWaves / wm - 1) * wm * 64 * 2;
+  return sizeof(uint32_t) * ((size_t)max_n + mask_rows * mask_words + merge);
+}
+
+// Workgroup shape: WM row groups of 32 rows, WM in {2, 4, 8}. A workgroup
+// needs enough rows for every wave to do useful work; with fewer rows the
+// eight waves split the keys of each step instead.
+int choose_wm(const dt_attn_desc* d, int g) {
+  int max_rows = 0;
+  for (int s = 0; s < d->num_seqs; ++s)
+    max_rows = std::max(max_rows, (d->node_offsets[s + 1] - d->node_offsets[s]) * g);
+  if (max_rows <= 64) return 2;
+  if (max_rows <= 128) return 4;
+  return 8;
+}
+
+// Keys per split for a given workgroup shape. Every work item streams at
+// most `chunk` keys; `chunk` is uniform, so items cost about the same and the
+// per-XCD item ranges balance. It is sized so that the items fill the CUs (one
+// workgroup each) about once.
+int64_t choose_chunk(const dt_attn_desc* d, int g, int rm, int cus) {
+  if (d->split_keys) return d->split_keys;
+  int64_t total_tiles = 0, max_keys = 0;
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int n = d->node_offsets[s + 1] - d->node_offsets[s];
+    const int64_t keys = (int64_t)d->prefix_lens[s] + n;
+    const int64_t units = ceil_div((int64_t)n * g, rm) * d->num_kv_heads;
+    total_tiles += units * ceil_div(keys, kBN);
+    max_keys = std::max(max_keys, keys);
+  }
+  const int64_t tiles = std::max<int64_t>(1, ceil_div(total_tiles, cus));
+  return std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
+}
+
+bool needs_split(const dt_attn_desc* d, int64_t chunk) {
+  for (int s = 0; s < d->num_seqs; ++s)
+    if ((int64_t)d->prefix_lens[s] + (d->node_offsets[s + 1] - d->node_offsets[s]) > chunk) return true;
+  return false;
+}
+
+bool lds_fits(int D, int wm, int max_n, int g) {
+  return static_lds_for(D, wm) + dynamic_lds(max_n, g, wm) <= (size_t)kLdsBytes;
 }
 
 int make_plan(const dt_attn_desc* d, Plan* plan) {
@@ -617,26 +867,21 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   if (st != DT_OK) return st;
   const int g = d->num_q_heads / d->num_kv_heads;
   const int D = d->head_dim;
+  int max_n = 1;
+  for (int s = 0; s < d->num_seqs; ++s) max_n = std::max(max_n, d->node_offsets[s + 1] - d->node_offsets[s]);
 
-  // Keys per split. Every work item streams at most `chunk` keys; `chunk` is
-  // uniform, so items cost about the same and the per-XCD item ranges balance.
-  // It is sized so that the items fill the GPU's workgroup slots (two per CU)
-  // about once, with at least kMinTiles key tiles per item to amortise the
-  // prologue (Q rows, ancestor masks) and keep the tile pipeline busy.
-  int64_t chunk = d->split_keys;
-  if (chunk == 0) {
-    int64_t total_tiles = 0, max_keys = 0;
-    for (int s = 0; s < d->num_seqs; ++s) {
-      const int n = d->node_offsets[s + 1] - d->node_offsets[s];
-      const int64_t keys = (int64_t)d->prefix_lens[s] + n;
-      const int64_t units = ceil_div((int64_t)n * g, kBM) * d->num_kv_heads;
-      total_tiles += units * ceil_div(keys, kBN);
-      max_keys = std::max(max_keys, keys);
-    }
-    const int64_t slots = 2LL * cus;
-    const int64_t tiles = std::max<int64_t>(kMinTiles, ceil_div(total_tiles, slots));
-    chunk = std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
-  }
+  // 256 rows per workgroup (the ping-pong schedule) unless 128 rows avoid
+  // splitting the keys where 256 would need it (e.g. ragged prefixes); fewer
+  // rows when the trees are small or the ancestor masks do not fit the LDS.
+  int wm = choose_wm(d, g);
+  if (wm == 8 && !d->split_keys && lds_fits(D, 4, max_n, g) &&
+      needs_split(d, choose_chunk(d, g, kWaveRows * 8, cus)) && !needs_split(d, choose_chunk(d, g, kWaveRows * 4, cus)))
+    wm = 4;
+  while (!lds_fits(D, wm, max_n, g) && wm > 2) wm /= 2;
+  if (!lds_fits(D, wm, max_n, g)) return DT_ERR_UNSUPPORTED;
+  plan->wm = wm;
+  const int rm = kWaveRows * wm;
+  int64_t chunk = choose_chunk(d, g, rm, cus);
   if (chunk > (int64_t)1 << 30) chunk = (int64_t)1 << 30;
 
   size_t part_rows = 0;
@@ -649,7 +894,7 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
     a.g = g;
     a.chunk = (int32_t)chunk;
     a.scale_log2 = d->softmax_scale * kLog2e;
-    int items = 0, comb = 0, max_n = 1;
+    int items = 0, comb = 0, launch_max_n = 1;
     for (int i = 0; i < a.nseq; ++i) {
       const int s = s0 + i;
       SeqGeom& sg = a.seq[i];
@@ -657,7 +902,7 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
       sg.n = d->node_offsets[s + 1] - d->node_offsets[s];
       sg.P = d->prefix_lens[s];
       sg.prefix_row0 = d->prefix_row_start[s];
-      sg.row_tiles = (int32_t)ceil_div((int64_t)sg.n * g, kBM);
+      sg.row_tiles = (int32_t)ceil_div((int64_t)sg.n * g, rm);
       sg.splits = (int32_t)std::max<int64_t>(1, ceil_div((int64_t)sg.P + sg.n, chunk));
       sg.item_start = items;
       items += sg.row_tiles * sg.splits * d->num_kv_heads;
@@ -670,25 +915,34 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
         sg.part_base = -1;
         sg.comb_start = -1;
       }
-      max_n = std::max(max_n, sg.n);
+      launch_max_n = std::max(launch_max_n, sg.n);
     }
     if (part_rows > (size_t)INT32_MAX) return DT_ERR_UNSUPPORTED;
     a.total_items = items;
     a.per_xcd = (int32_t)ceil_div(items, kXcds);
-    a.max_n = max_n;
-    a.mask_words = (max_n + 31) / 32 + 2;
-    a.mask_rows = (kBM - 1) / g + 2;
+    a.max_n = launch_max_n;
+    a.mask_words = (launch_max_n + 31) / 32 + 2;
+    a.mask_rows = (rm - 1) / g + 2;
     a.comb_rows = comb;
     plan->launches.push_back(a);
     plan->grid.push_back(a.per_xcd * kXcds);
     plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 4)) : 0);
-    plan->lds.push_back(sizeof(uint32_t) * ((size_t)a.max_n + (size_t)a.mask_rows * a.mask_words));
+    plan->lds.push_back(dynamic_lds(launch_max_n, g, wm));
   }
-  (void)D;
   plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(float), 256) +
                                    round_up(part_rows * sizeof(float2), 256)
                              : 0;
   return DT_OK;
+}
+
+template <int D>
+void launch_fwd(int wm, int grid, size_t lds, hipStream_t st, const AttnParams& a) {
+  if (wm == 8)
+    hipLaunchKernelGGL((tree_attn_fwd<D, 8>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (wm == 4)
+    hipLaunchKernelGGL((tree_attn_fwd<D, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((tree_attn_fwd<D, 2>), dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 }  // namespace
@@ -758,10 +1012,10 @@ extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const 
     a.p_hs = desc->prefix_head_stride;
     if (a.total_items == 0) continue;
     if (D == 128) {
-      hipLaunchKernelGGL(tree_attn_fwd<128>, dim3(plan.grid[li]), dim3(kThreads), plan.lds[li], st_, a);
+      launch_fwd<128>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
       if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<128>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
     } else {
-      hipLaunchKernelGGL(tree_attn_fwd<64>, dim3(plan.grid[li]), dim3(kThreads), plan.lds[li], st_, a);
+      launch_fwd<64>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
       if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<64>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
     }
     st = launch_status();
