@@ -36,7 +36,8 @@
 //    parent[i] < i, tree keys beyond the workgroup's last node are skipped.
 //  * When there are too few (sequence, KV head, row tile) units to occupy the
 //    GPU, each unit's keys are split into chunks; partial (O, m, l) go to the
-//    workspace and a second kernel merges them with log-sum-exp weights.
+//    workspace (O as fp16 after an exact power-of-two scaling per row) and a
+//    second kernel merges them with log-sum-exp weights.
 //  * Work items are ordered so that the row tiles sharing one key chunk are
 //    dispatched to the same XCD (workgroups go round-robin over the 8 XCDs),
 //    which keeps that chunk's K/V in one L2.
@@ -96,8 +97,8 @@ struct AttnParams {
   const bf16_bits* vp;
   const int32_t* parent;
   bf16_bits* out;
-  float* part_o;   // [part rows][D] unnormalised partial outputs
-  float2* part_ml; // [part rows] (running max in log2 units, sum)
+  _Float16* part_o;  // [part rows][D] unnormalised partial outputs times 2^-e (|values| < 1)
+  float4* part_ml;   // [part rows] (running max in log2 units, sum, 2^e, unused)
   int64_t q_rs, out_rs, t_rs, p_rs, p_hs;
   float scale_log2;
   int32_t Hq, Hkv, g;
@@ -691,15 +692,30 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         *reinterpret_cast<uint2*>(orow + i * 32 + j4 * 8 + hh * 4) = *reinterpret_cast<uint2*>(o4);
       }
   } else {
-    const int64_t prow = (int64_t)sg.part_base + ((int64_t)split * sg.n + my_node) * p.Hq + my_qh;
-    float* po = p.part_o + prow * D;
+    // Partial for the merge: the row's unnormalised output scaled by a power
+    // of two 2^-e so that every |value| < 1, stored as fp16 (an exact scaling,
+    // so the stored values keep 11 significant bits relative to the row's
+    // largest entry whatever the magnitude of V), with (m, l, 2^e).
+    float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4)
-        *reinterpret_cast<float4*>(po + i * 32 + j4 * 8 + hh * 4) =
-            make_float4(acc[i][j4 * 4], acc[i][j4 * 4 + 1], acc[i][j4 * 4 + 2], acc[i][j4 * 4 + 3]);
-    if (hh == 0) p.part_ml[prow] = make_float2(m_run, l_tot);
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(acc[i][j]));
+    amax = max_halves(amax);
+    const int e = min(((int)((__float_as_uint(amax) >> 23) & 255)) - 126, 127);  // amax < 2^e (or e = 127)
+    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    const int64_t prow = (int64_t)sg.part_base + ((int64_t)split * sg.n + my_node) * p.Hq + my_qh;
+    _Float16* po = p.part_o + prow * D;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        _Float16 h4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h4[q] = (_Float16)(acc[i][j4 * 4 + q] * down);
+        *reinterpret_cast<uint2*>(po + i * 32 + j4 * 8 + hh * 4) = *reinterpret_cast<uint2*>(h4);
+      }
+    if (hh == 0) p.part_ml[prow] = make_float4(m_run, l_tot, __builtin_amdgcn_ldexpf(1.f, e), 0.f);
   }
 }
 
@@ -724,15 +740,15 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   // partial row of chunk k: part_base + (k * n + node) * Hq + qh = part_base + r + k * n * Hq
   const int64_t prow0 = (int64_t)sg.part_base + r;
   const int64_t kstride = (int64_t)sg.n * p.Hq;
-  const float4* po = reinterpret_cast<const float4*>(p.part_o);
+  const uint2* po = reinterpret_cast<const uint2*>(p.part_o);  // four fp16 values per thread
   // One pass with a running maximum; chunks are loaded eight at a time so
   // that their loads are in flight together.
   constexpr int kBatch = 8;
   float m = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k0 = 0; k0 < sg.splits; k0 += kBatch) {
-    float2 ml[kBatch];
-    float4 v[kBatch];
+    float4 ml[kBatch];
+    uint2 v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int k = min(k0 + u, sg.splits - 1);
@@ -747,11 +763,13 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
         const float mn = fmaxf(m, ml[u].x);
         const float a = __builtin_amdgcn_exp2f(m - mn);
         const float w = __builtin_amdgcn_exp2f(ml[u].x - mn);
+        const float ws = w * ml[u].z;  // undoes the stored 2^-e
+        const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
         l = l * a + w * ml[u].y;
-        o.x = o.x * a + w * v[u].x;
-        o.y = o.y * a + w * v[u].y;
-        o.z = o.z * a + w * v[u].z;
-        o.w = o.w * a + w * v[u].w;
+        o.x = o.x * a + ws * (float)h[0];
+        o.y = o.y * a + ws * (float)h[1];
+        o.z = o.z * a + ws * (float)h[2];
+        o.w = o.w * a + ws * (float)h[3];
         m = mn;
       }
     }
@@ -929,8 +947,8 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
     plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 4)) : 0);
     plan->lds.push_back(dynamic_lds(launch_max_n, g, wm));
   }
-  plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(float), 256) +
-                                   round_up(part_rows * sizeof(float2), 256)
+  plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(_Float16), 256) +
+                                   round_up(part_rows * sizeof(float4), 256)
                              : 0;
   return DT_OK;
 }
@@ -987,10 +1005,10 @@ extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const 
       if (a.seq[i].splits > 1)
         part_rows_bytes = std::max(part_rows_bytes,
                                    (size_t)(a.seq[i].part_base + (size_t)a.seq[i].splits * a.seq[i].n * a.Hq));
-  float* part_o = static_cast<float*>(workspace);
-  float2* part_ml = plan.ws_bytes
-                        ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                                    round_up(part_rows_bytes * D * sizeof(float), 256))
+  _Float16* part_o = static_cast<_Float16*>(workspace);
+  float4* part_ml = plan.ws_bytes
+                        ? reinterpret_cast<float4*>(static_cast<char*>(workspace) +
+                                                    round_up(part_rows_bytes * D * sizeof(_Float16), 256))
                         : nullptr;
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);

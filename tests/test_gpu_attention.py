@@ -108,6 +108,22 @@ def test_forced_key_splits(split):
     assert_attention_close(host_f64(out), _oracle(ops, parents, [100], [1000]), what=f"split {split}")
 
 
+@pytest.mark.parametrize("v_scale", [1e-3, 3e3])
+def test_split_partials_keep_precision_at_any_magnitude(v_scale):
+    """Split sequences merge per-chunk partials; the merge must be exact up to
+    rounding whatever the magnitude of V (the result is linear in V)."""
+    require_gpu()
+    parents, ops = _case([120], [900], 8, 2, 128, ["deep"], seed=13, scale=0.7)
+    ops = dict(ops)
+    for key in ("v_tree", "v_prefix"):
+        ops[key] = gten.bf16_round(ops[key] * np.float32(v_scale))
+    print(f"split partials v_scale={v_scale}", flush=True)
+    for split in (64, 320):
+        out, _ = _run(ops, parents, [120], [900], 8, 2, 128, split_keys=split)
+        assert_attention_close(host_f64(out), _oracle(ops, parents, [120], [900]), atol=2e-2 * max(v_scale, 1.0),
+                               what=f"v_scale={v_scale} split={split}")
+
+
 def test_ragged_batch_strided_cache():
     """Five sequences with different prefixes and trees; the prefix cache is
     head-major [Hkv][rows][d] with gaps between the sequences' rows."""
