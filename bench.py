@@ -144,10 +144,16 @@ class Round:
         if st != 0:
             raise self.dt.DtError(st, "dt_tree_attention")
 
-    def step(self):
+    def step(self, events=None):
+        """One round. `events` (start, end), if given, bracket the round's
+        attention calls on the stream they run on."""
         t = self.build_and_upload()
+        if events is not None:
+            events[0].record()
         for l in range(self.w.layers):
             self.attention(l)
+        if events is not None:
+            events[1].record()
         lg = self.logits[t]
         st = self.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), self.am.data_ptr(),
                                      self.ws_am.data_ptr(), self.ws_am.numel(), self.stream)
@@ -167,18 +173,35 @@ class Round:
         return flops(self.w.nodes, self.w.prefix_lens, [p for p, _, _, _ in self.trees[table]], self.w.Hq, self.w.d)
 
 
-def time_attention_calls(rnd, reps):
-    """Average duration of one dt_tree_attention call, from HIP events recorded
-    on the stream the kernels run on."""
-    torch = rnd.torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        evs[i][0].record()
-        rnd.attention(i % rnd.w.layers)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return float(np.mean(ms)), float(np.median(ms))
+def attention_bytes(w):
+    """Algorithmic bytes of one call: prefix K and V once, plus per node Q, O,
+    tree K and V, and the parent index."""
+    kv = sum(2 * P * w.Hkv * w.d * 2 for P in w.prefix_lens)
+    per_node = 2 * w.Hq * w.d * 2 + 2 * w.Hkv * w.d * 2 + 4
+    return int(kv + w.total_nodes * per_node)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attn_hbm_traffic.json")
+
+
+def recorded_traffic(w):
+    """HBM bytes per dt_tree_attention call measured with the FETCH_SIZE and
+    WRITE_SIZE counters (profiles/), valid only for the attention source they
+    were taken on and for this workload."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src = os.path.join(ROOT, "draft_tree_verification_dt_amd", "csrc", "attention.hip")
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(w.name)
+    if rec.get("attention_source_sha256") != digest or entry is None:
+        return None
+    return {"bytes_per_launch": entry["bytes_per_launch"], "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
 
 def time_argmax_calls(rnd, reps):
@@ -305,22 +328,27 @@ def main():
     for _ in range(args.warmup):
         rnd.step()
     torch.cuda.synchronize()
+    # the timed region; HIP events on the kernels' stream bracket each step's attention calls
+    att_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        rnd.step()
+    for i in range(args.steps):
+        rnd.step(att_events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
+    att_call_ms = [a.elapsed_time(b) / w.layers for a, b in att_events]  # one dt_tree_attention call
 
     flops_layer = float(np.mean([rnd.attention_flops(t) for t in range(N_TABLES)]))
     round_flops = flops_layer * w.layers
     value = round_flops / (ms_per_step / 1e3) / 1e12
 
     parity = None if args.no_parity else parity_check(rnd)  # checks the last timed step's outputs
-    att_mean_ms, att_med_ms = time_attention_calls(rnd, reps=max(2 * w.layers, 36))
+    att_mean_ms = float(np.mean(att_call_ms))
     arg_ms = time_argmax_calls(rnd, reps=10)
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
+    traffic = recorded_traffic(w)
 
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -330,10 +358,14 @@ def main():
                    "tree_nodes": w.nodes[0] if len(set(w.nodes)) == 1 else w.nodes, "layers": w.layers,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "vocab": w.vocab, "tree": w.tree},
         "us_per_round": round(ms_per_step * 1e3, 1),
-        "roofline": {"bound": "mfma", "kernel": "dt_tree_attention (tree_attn_fwd + tree_attn_combine)",
+        "roofline": {"bound": "mfma", "kernel": "dt_tree_attention call (tree_attn_fwd + tree_attn_combine)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "flops_per_launch": flops_layer, "launch_ms_mean": att_mean_ms, "launch_ms_median": att_med_ms},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "flops_per_launch": flops_layer, "launch_us_mean": round(att_mean_ms * 1e3, 2),
+                     "launch_us_median": round(float(np.median(att_call_ms)) * 1e3, 2),
+                     "algorithmic_bytes_per_launch": attention_bytes(w),
+                     "traffic_source": traffic["source"] if traffic else None},
         "argmax": {"ms": arg_ms, "GB/s": argmax_bytes / (arg_ms / 1e3) / 1e9,
                    "frac_hbm": argmax_bytes / (arg_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "parity": parity,
