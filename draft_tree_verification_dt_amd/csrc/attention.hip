@@ -719,15 +719,15 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   }
 }
 
-// Merge the per-chunk partials of split sequences. A thread owns four
-// consecutive dims of one (node, query head) row, so the threads of a row read
-// each chunk's partial as one contiguous line.
+// Merge the per-chunk partials of split sequences. A thread owns eight
+// consecutive dims of one (node, query head) row (one 16-byte load per chunk),
+// so the threads of a row read each chunk's partial as one contiguous line.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
-  constexpr int kTpr = D / 4;          // threads per row
+  constexpr int kTpr = D / 8;          // threads per row
   constexpr int kRpb = 256 / kTpr;     // rows per block
   const int row = blockIdx.x * kRpb + threadIdx.x / kTpr;
-  const int c4 = threadIdx.x % kTpr;
+  const int c8 = threadIdx.x % kTpr;
   if (row >= p.comb_rows) return;
   int s = -1;
   for (int i = 0; i < p.nseq; ++i)
@@ -740,44 +740,53 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   // partial row of chunk k: part_base + (k * n + node) * Hq + qh = part_base + r + k * n * Hq
   const int64_t prow0 = (int64_t)sg.part_base + r;
   const int64_t kstride = (int64_t)sg.n * p.Hq;
-  const uint2* po = reinterpret_cast<const uint2*>(p.part_o);  // four fp16 values per thread
-  // One pass with a running maximum; chunks are loaded eight at a time so
-  // that their loads are in flight together.
+  const uint4* po = reinterpret_cast<const uint4*>(p.part_o);  // eight fp16 values per thread
+  // Chunks are merged eight at a time (their loads in flight together): the
+  // batch's maximum first, then every chunk with one weight.
   constexpr int kBatch = 8;
   float m = -INFINITY, l = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < sg.splits; k0 += kBatch) {
     float4 ml[kBatch];
-    uint2 v[kBatch];
+    uint4 v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int k = min(k0 + u, sg.splits - 1);
       const int64_t prow = prow0 + k * kstride;
       ml[u] = p.part_ml[prow];
-      v[u] = po[prow * kTpr + c4];
+      v[u] = po[prow * kTpr + c8];
     }
+    // a chunk that saw no visible key for this row (l = 0) contributes nothing
+    bool ok[kBatch];
+    float mb = m;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      // a chunk that saw no visible key for this row (l = 0) contributes nothing
-      if (k0 + u < sg.splits && ml[u].y > 0.f) {
-        const float mn = fmaxf(m, ml[u].x);
-        const float a = __builtin_amdgcn_exp2f(m - mn);
-        const float w = __builtin_amdgcn_exp2f(ml[u].x - mn);
-        const float ws = w * ml[u].z;  // undoes the stored 2^-e
-        const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
-        l = l * a + w * ml[u].y;
-        o.x = o.x * a + ws * (float)h[0];
-        o.y = o.y * a + ws * (float)h[1];
-        o.z = o.z * a + ws * (float)h[2];
-        o.w = o.w * a + ws * (float)h[3];
-        m = mn;
-      }
+      ok[u] = k0 + u < sg.splits && ml[u].y > 0.f;
+      if (ok[u]) mb = fmaxf(mb, ml[u].x);
+    }
+    if (mb == -INFINITY) continue;  // nothing visible yet
+    const float a = __builtin_amdgcn_exp2f(m - mb);  // 0 on the first visible batch
+    l *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= a;
+    m = mb;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (!ok[u]) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - m);
+      const float ws = w * ml[u].z;  // undoes the stored 2^-e
+      const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
+      l += w * ml[u].y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += ws * (float)h[e];
     }
   }
   const float inv = 1.f / l;
-  __bf16 o4[4] = {(__bf16)(o.x * inv), (__bf16)(o.y * inv), (__bf16)(o.z * inv), (__bf16)(o.w * inv)};
-  bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + c4 * 4;
-  *reinterpret_cast<uint2*>(orow) = *reinterpret_cast<uint2*>(o4);
+  __bf16 o8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(o[e] * inv);
+  bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + c8 * 8;
+  *reinterpret_cast<uint4*>(orow) = *reinterpret_cast<uint4*>(o8);
 }
 
 // ---------------------------------------------------------------- host side
@@ -892,9 +901,16 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   // splitting the keys where 256 would need it (e.g. ragged prefixes); fewer
   // rows when the trees are small or the ancestor masks do not fit the LDS.
   int wm = choose_wm(d, g);
-  if (wm == 8 && !d->split_keys && lds_fits(D, 4, max_n, g) &&
-      needs_split(d, choose_chunk(d, g, kWaveRows * 8, cus)) && !needs_split(d, choose_chunk(d, g, kWaveRows * 4, cus)))
-    wm = 4;
+  // 128-row tiles instead of 256-row ones when that avoids the key split, or
+  // when the split would leave each workgroup at most eight steps: there the
+  // split partials' round trip (written by every chunk, read back by the
+  // merge) costs more than the shorter tiles, and 128-row tiles halve it.
+  if (wm == 8 && !d->split_keys && lds_fits(D, 4, max_n, g)) {
+    const int64_t chunk8 = choose_chunk(d, g, kWaveRows * 8, cus);
+    if (needs_split(d, chunk8) &&
+        (!needs_split(d, choose_chunk(d, g, kWaveRows * 4, cus)) || chunk8 <= 8 * kBN))
+      wm = 4;
+  }
   while (!lds_fits(D, wm, max_n, g) && wm > 2) wm /= 2;
   if (!lds_fits(D, wm, max_n, g)) return DT_ERR_UNSUPPORTED;
   plan->wm = wm;
@@ -944,7 +960,7 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
     a.comb_rows = comb;
     plan->launches.push_back(a);
     plan->grid.push_back(a.per_xcd * kXcds);
-    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 4)) : 0);
+    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8)) : 0);
     plan->lds.push_back(dynamic_lds(launch_max_n, g, wm));
   }
   plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(_Float16), 256) +
