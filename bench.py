@@ -204,6 +204,20 @@ def recorded_traffic(w):
     return {"bytes_per_launch": entry["bytes_per_launch"], "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
 
+def tree_shape(rnd):
+    """Realized shape of the round's trees (the candidate tables cap the depth at
+    the number of draft positions; the best-first order decides how deep the
+    trees actually grow): node-depth histogram summed over all tables and
+    sequences, and the deepest node."""
+    hist = {}
+    for trees in rnd.trees:
+        for _, _, depth, _ in trees:
+            for dd, c in zip(*np.unique(depth, return_counts=True)):
+                hist[int(dd)] = hist.get(int(dd), 0) + int(c)
+    return {"depth_hist": [hist.get(i, 0) for i in range(max(hist) + 1)], "max_depth": max(hist),
+            "tables": len(rnd.trees)}
+
+
 def time_argmax_calls(rnd, reps):
     torch = rnd.torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -369,6 +383,7 @@ def main():
         "argmax": {"ms": arg_ms, "GB/s": argmax_bytes / (arg_ms / 1e3) / 1e9,
                    "frac_hbm": argmax_bytes / (arg_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "parity": parity,
+        "trees": tree_shape(rnd),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(rnd, args.cpu_budget_s)
