@@ -16,6 +16,11 @@ What it computes, and where the pages define it:
 * ``argmax``     -- the target's greedy prediction per node, lowest index on
                     ties (DARTree paper, Preliminaries > Speculative Sampling,
                     the T = 0 rule).
+* ``sample``     -- the target's sample per node at temperature T > 0 for
+                    exact target-sample matching (DARTree paper, Preliminaries >
+                    Speculative Sampling, the DFlash rule; Experimental Setup >
+                    Evaluation Details at T = 1), drawn by Gumbel-max from
+                    Philox4x32-10 uniforms.
 * ``walk``       -- the accepted root-to-leaf path and the bonus token (same
                     passage, plus the bonus-token sentence of Speculative
                     Sampling and the definition of tau in Experimental Setup).
@@ -29,4 +34,4 @@ something other than itself (library routines, closed forms, brute force,
 hand-worked fixtures under tests/golden/). No function is left unpinned.
 """
 
-from . import tree, attention, argmax, walk, build_tree  # noqa: F401
+from . import tree, attention, argmax, sample, walk, build_tree  # noqa: F401
