@@ -8,6 +8,7 @@ in libdtree (host C++ for the tree builder, HIP kernels for the rest).
     dt_build_tree       best-first (DDTree) draft-tree construction, host
     dt_tree_attention   ancestor-only tree attention over a KV-cached prefix
     dt_argmax_rows      per-node greedy prediction (row arg-max, lowest index on ties)
+    dt_sample_rows      per-node target sample at temperature T > 0 (Gumbel-max, Philox4x32-10)
     dt_accept_path      longest accepted root-to-leaf path and bonus token
 """
 
@@ -21,7 +22,8 @@ from ._lib import dt_attn_desc  # noqa: F401
 __all__ = [
     "DtError", "dt_status_string", "dt_abi_version", "dt_build_tree", "dt_validate_tree",
     "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention",
-    "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_accept_path", "library_path",
+    "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_sample_rows_workspace_size", "dt_sample_rows",
+    "dt_accept_path", "library_path",
 ]
 
 
@@ -220,6 +222,36 @@ def dt_argmax_rows(logits, out=None, workspace=None, stream=None):
     st = _lib.load().dt_argmax_rows(logits.data_ptr(), rows, vocab, logits.stride(0), out.data_ptr(), ws_ptr, ws_len,
                                     _stream(stream))
     _check(st, "dt_argmax_rows")
+    return out
+
+
+def dt_sample_rows_workspace_size(rows, vocab):
+    n = ctypes.c_size_t(0)
+    _check(_lib.load().dt_sample_rows_workspace_size(int(rows), int(vocab), ctypes.byref(n)),
+           "dt_sample_rows_workspace_size")
+    return n.value
+
+
+def dt_sample_rows(logits, temperature, seed, offset, out=None, workspace=None, stream=None):
+    """Per-row sample from softmax(logits / temperature) by Gumbel-max with
+    Philox4x32-10 noise keyed by (seed, offset, row, vocabulary index), for a
+    [rows, vocab] float32 CUDA tensor with unit column stride. Returns int32 [rows]."""
+    import torch
+
+    rows, vocab = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits: vocab dimension must be contiguous")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    need = dt_sample_rows_workspace_size(rows, vocab)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dt_sample_rows(logits.data_ptr(), rows, vocab, logits.stride(0), float(temperature),
+                                    int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFFFFFFFFFF, out.data_ptr(),
+                                    ws_ptr, ws_len, _stream(stream))
+    _check(st, "dt_sample_rows")
     return out
 
 

@@ -60,6 +60,9 @@ SIGNATURES = {
     "dt_tree_attention": (ctypes.c_int, [ctypes.POINTER(dt_attn_desc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_size, c_p]),
     "dt_argmax_rows_workspace_size": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_size)]),
     "dt_argmax_rows": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_size, c_p]),
+    "dt_sample_rows_workspace_size": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_size)]),
+    "dt_sample_rows": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, c_p,
+                                      c_p, c_size, c_p]),
     "dt_accept_path": (ctypes.c_int, [c_i32, P_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
 }
 

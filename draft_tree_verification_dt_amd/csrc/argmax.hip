@@ -1,5 +1,8 @@
 // Row-wise arg-max of fp32 target logits: the target's greedy prediction at
-// every tree node (DARTree paper, Preliminaries > Speculative Sampling, T = 0).
+// every tree node (DARTree paper, Preliminaries > Speculative Sampling, T = 0),
+// and the same scan over Gumbel-perturbed logits: the target's sample at every
+// node for exact target-sample matching at T > 0 (same passage, the DFlash
+// rule; Experimental Setup > Evaluation Details, T = 1).
 //
 // Pure streaming work, bound by HBM bandwidth. Each row is cut into chunks so
 // that the launch has enough workgroups whatever the row count (a 16-node
@@ -9,11 +12,25 @@
 // shuffles and the four waves through LDS. With one chunk per row the result
 // is written directly; otherwise per-chunk (value, index) pairs go to the
 // workspace and a second kernel merges them. Ties go to the lowest index.
+//
+// Sampling (Gumbel-max): argmax_j (l_j / T - ln(-ln U_j)) is an exact draw from
+// softmax(l / T). The uniforms come from Philox4x32-10 (Salmon et al., "Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011) with counter
+// (row, j / 4, offset_lo, offset_hi) and key (seed_lo, seed_hi); word j % 4 of
+// the output block gives U_j = (2 * (word >> 9) + 1) * 2^-24. One Philox call
+// covers the four entries of a 16-byte load. The kernel compares, in fp32,
+//   s_j = l_j * (log2(e) / T) - log2(-log2 U_j),
+// which is the natural-log score times log2(e) minus a constant, so it ranks
+// the vocabulary exactly as the definition does (up to fp32 rounding). Two of
+// the counter words and the key are uniform across a workgroup, so the first
+// rounds partly run on the scalar unit. Ten rounds of two 32x32->64-bit
+// multiplies per four entries make this variant ALU-bound rather than HBM-bound.
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <climits>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -27,6 +44,62 @@ constexpr int kUnroll = 4;
 constexpr int64_t kChunkQuantum = 4 * kThreads * kUnroll;  // elements; keeps chunks 16-byte aligned
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Sampling parameters passed by value; unused by the greedy variant.
+struct Gumbel {
+  float c;         // log2(e) / T
+  uint32_t k0, k1; // Philox key: seed low and high words
+  uint32_t o0, o1; // counter words 2 and 3: offset low and high words
+};
+
+// Philox4x32-10 of counter (c0, c1, c2, c3) and key (k0, k1), in place.
+__device__ inline void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                     uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    // three-input XOR in one VALU op (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+}
+
+// The four Philox words of vocabulary block j (entries 4j .. 4j+3) of a row.
+__device__ inline void gumbel_block(const Gumbel& g, uint32_t row, uint32_t j, uint32_t w[4]) {
+  uint32_t c0 = row, c1 = j, c2 = g.o0, c3 = g.o1;
+  philox4x32_10(c0, c1, c2, c3, g.k0, g.k1);
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+}
+
+// s = l * log2(e)/T - log2(-log2 U), U = (2 * (w >> 9) + 1) * 2^-24. The
+// subtraction is exact: 1 + k 2^-23 minus (1 - 2^-24) is (2k + 1) 2^-24. Both
+// logarithms see normal inputs (U >= 2^-24, -log2 U >= 8.5e-8).
+__device__ inline float gumbel_score(float l, uint32_t w, float c) {
+  const float u = __uint_as_float(0x3F800000u | (w >> 9)) - __uint_as_float(0x3F7FFFFFu);
+  const float e = -__builtin_amdgcn_logf(u);
+  return fmaf(l, c, -__builtin_amdgcn_logf(e));
+}
+
+// A thread visits its entries in increasing index order, so within a thread a
+// strictly larger value is the only way to improve (the lowest index of a tie
+// is already held). Across threads and chunks the index breaks ties.
+#define TAKE_IF_LARGER(val, idx) \
+  if ((val) > bv) {              \
+    bv = (val);                  \
+    bi = (idx);                  \
+  }
 
 // Is (v, i) a better arg-max candidate than (bv, bi)? Larger value, then lower index.
 __device__ inline bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
@@ -62,11 +135,34 @@ __device__ inline void block_reduce(float& bv, int& bi) {
   }
 }
 
-// grid: (chunks, rows). VEC: row starts are 16-byte aligned.
-template <bool VEC>
+// Value compared for entry t of a row: the logit, or its Gumbel score.
+template <bool SAMPLE>
+__device__ inline float entry_value(float l, int64_t t, uint32_t row, const Gumbel& g) {
+  if (!SAMPLE) return l;
+  uint32_t w[4];
+  gumbel_block(g, row, (uint32_t)(t >> 2), w);
+  const int k = (int)(t & 3);
+  const uint32_t wk = k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+  return gumbel_score(l, wk, g.c);
+}
+
+// Gumbel scores of the four entries of vocabulary block j.
+__device__ inline f32x4 gumbel4(f32x4 v, uint32_t row, uint32_t j, const Gumbel& g) {
+  uint32_t w[4];
+  gumbel_block(g, row, j, w);
+  v.x = gumbel_score(v.x, w[0], g.c);
+  v.y = gumbel_score(v.y, w[1], g.c);
+  v.z = gumbel_score(v.z, w[2], g.c);
+  v.w = gumbel_score(v.w, w[3], g.c);
+  return v;
+}
+
+// grid: (chunks, rows). VEC: row starts are 16-byte aligned. SAMPLE: compare
+// Gumbel scores instead of logits.
+template <bool VEC, bool SAMPLE>
 __global__ __launch_bounds__(kThreads) void argmax_chunks(const float* __restrict__ x, int64_t vocab, int64_t stride,
                                                           int64_t chunk_len, int chunks, int32_t* __restrict__ out_idx,
-                                                          float2* __restrict__ part) {
+                                                          float2* __restrict__ part, const Gumbel g) {
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   const float* xr = x + row * stride;
@@ -85,30 +181,36 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const float* __restric
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int base = (int)((j + u * kThreads) << 2);
-        if (better(v[u].x, base, bv, bi)) { bv = v[u].x; bi = base; }
-        if (better(v[u].y, base + 1, bv, bi)) { bv = v[u].y; bi = base + 1; }
-        if (better(v[u].z, base + 2, bv, bi)) { bv = v[u].z; bi = base + 2; }
-        if (better(v[u].w, base + 3, bv, bi)) { bv = v[u].w; bi = base + 3; }
+        if (SAMPLE) v[u] = gumbel4(v[u], (uint32_t)row, (uint32_t)(j + u * kThreads), g);
+        TAKE_IF_LARGER(v[u].x, base);
+        TAKE_IF_LARGER(v[u].y, base + 1);
+        TAKE_IF_LARGER(v[u].z, base + 2);
+        TAKE_IF_LARGER(v[u].w, base + 3);
       }
     }
     for (; j < end4; j += kThreads) {
-      const f32x4 v = __builtin_nontemporal_load(x4 + j);
+      f32x4 v = __builtin_nontemporal_load(x4 + j);
       const int base = (int)(j << 2);
-      if (better(v.x, base, bv, bi)) { bv = v.x; bi = base; }
-      if (better(v.y, base + 1, bv, bi)) { bv = v.y; bi = base + 1; }
-      if (better(v.z, base + 2, bv, bi)) { bv = v.z; bi = base + 2; }
-      if (better(v.w, base + 3, bv, bi)) { bv = v.w; bi = base + 3; }
+      if (SAMPLE) v = gumbel4(v, (uint32_t)row, (uint32_t)j, g);
+      TAKE_IF_LARGER(v.x, base);
+      TAKE_IF_LARGER(v.y, base + 1);
+      TAKE_IF_LARGER(v.z, base + 2);
+      TAKE_IF_LARGER(v.w, base + 3);
     }
-    for (int64_t t = (end4 << 2) + threadIdx.x; t < end; t += kThreads)
-      if (better(xr[t], (int)t, bv, bi)) { bv = xr[t]; bi = (int)t; }
+    for (int64_t t = (end4 << 2) + threadIdx.x; t < end; t += kThreads) {
+      const float v = entry_value<SAMPLE>(xr[t], t, (uint32_t)row, g);
+      TAKE_IF_LARGER(v, (int)t);
+    }
   } else {
-    for (int64_t t = beg + threadIdx.x; t < end; t += kThreads)
-      if (better(xr[t], (int)t, bv, bi)) { bv = xr[t]; bi = (int)t; }
+    for (int64_t t = beg + threadIdx.x; t < end; t += kThreads) {
+      const float v = entry_value<SAMPLE>(xr[t], t, (uint32_t)row, g);
+      TAKE_IF_LARGER(v, (int)t);
+    }
   }
   block_reduce(bv, bi);
   if (threadIdx.x == 0) {
     if (chunks == 1) {
-      out_idx[row] = (bi >= 0 && bi < vocab) ? bi : 0;  // only a NaN-filled row leaves bi unset
+      out_idx[row] = (bi >= 0 && bi < vocab) ? bi : 0;  // bi stays unset only when no entry exceeds -inf (all -inf, or NaN): index 0
     } else {
       float2 r;
       r.x = bv;
@@ -165,14 +267,11 @@ extern "C" int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t
   return DT_OK;
 }
 
-extern "C" int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t* out_idx,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace dt;
-  if (rows < 0 || vocab < 1 || vocab > INT_MAX || row_stride < vocab) return DT_ERR_SHAPE;
-  if (rows > 65535) return DT_ERR_UNSUPPORTED;
-  if (rows == 0) return DT_OK;
-  if (!logits || !out_idx) return DT_ERR_NULL;
-  if (!aligned(logits, 4) || !aligned(out_idx, 4)) return DT_ERR_SHAPE;
+namespace dt {
+namespace {
+
+int launch_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t* out_idx,
+                void* workspace, size_t workspace_bytes, void* stream, bool sample, const Gumbel& g) {
   int cus = 0;
   int st = current_device_cus(&cus);
   if (st != DT_OK) return st;
@@ -189,11 +288,64 @@ extern "C" int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = aligned(logits, 16) && (row_stride % 4 == 0);
   dim3 grid((unsigned)chunks, (unsigned)rows);
-  if (vec)
-    hipLaunchKernelGGL(argmax_chunks<true>, grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len, chunks, out_idx, part);
-  else
-    hipLaunchKernelGGL(argmax_chunks<false>, grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len, chunks, out_idx, part);
+  if (sample) {
+    if (vec)
+      hipLaunchKernelGGL((argmax_chunks<true, true>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len, chunks,
+                         out_idx, part, g);
+    else
+      hipLaunchKernelGGL((argmax_chunks<false, true>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
+                         chunks, out_idx, part, g);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((argmax_chunks<true, false>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
+                         chunks, out_idx, part, g);
+    else
+      hipLaunchKernelGGL((argmax_chunks<false, false>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
+                         chunks, out_idx, part, g);
+  }
   if (chunks > 1)
     hipLaunchKernelGGL(argmax_merge, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, rows, vocab, chunks, part, out_idx);
   return launch_status();
+}
+
+int check_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, const int32_t* out_idx) {
+  if (rows < 0 || vocab < 1 || vocab > INT_MAX || row_stride < vocab) return DT_ERR_SHAPE;
+  if (rows > 65535) return DT_ERR_UNSUPPORTED;
+  if (rows == 0) return DT_OK;
+  if (!logits || !out_idx) return DT_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(out_idx, 4)) return DT_ERR_SHAPE;
+  return DT_OK;
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t* out_idx,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = dt::check_rows(logits, rows, vocab, row_stride, out_idx);
+  if (st != DT_OK || rows == 0) return st;
+  return dt::launch_rows(logits, rows, vocab, row_stride, out_idx, workspace, workspace_bytes, stream, false,
+                         dt::Gumbel{});
+}
+
+extern "C" int dt_sample_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
+  return dt_argmax_rows_workspace_size(rows, vocab, bytes);
+}
+
+extern "C" int dt_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, float temperature,
+                              uint64_t seed, uint64_t offset, int32_t* out_idx, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const int st = dt::check_rows(logits, rows, vocab, row_stride, out_idx);
+  if (st != DT_OK) return st;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return DT_ERR_VALUE;
+  const double c = 1.4426950408889634 / (double)temperature;  // log2(e) / T
+  if (!(c <= (double)FLT_MAX)) return DT_ERR_VALUE;
+  if (rows == 0) return DT_OK;
+  dt::Gumbel g;
+  g.c = (float)c;
+  g.k0 = (uint32_t)seed;
+  g.k1 = (uint32_t)(seed >> 32);
+  g.o0 = (uint32_t)offset;
+  g.o1 = (uint32_t)(offset >> 32);
+  return dt::launch_rows(logits, rows, vocab, row_stride, out_idx, workspace, workspace_bytes, stream, true, g);
 }

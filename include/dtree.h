@@ -16,6 +16,7 @@
  *   dt_build_tree       host: best-first (DDTree) tree construction
  *   dt_tree_attention   GPU:  ancestor-only tree attention over a KV-cached prefix
  *   dt_argmax_rows      GPU:  per-node greedy prediction (row arg-max)
+ *   dt_sample_rows      GPU:  per-node target sample at temperature T > 0 (Gumbel-max)
  *   dt_accept_path      GPU:  longest accepted path and bonus token
  *
  * Conventions shared by every entry point
@@ -208,14 +209,55 @@ int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes);
  *   logits     device float32, rows x vocab, row stride row_stride >= vocab;
  *              4-byte aligned. Contract: finite values (a NaN gives an
  *              unspecified index in [0, vocab)).
- *   rows >= 0 (0 is a no-op), 1 <= vocab < 2^31
+ *   rows >= 0 (0 is a no-op; at most 65535), 1 <= vocab < 2^31
  *   out_idx    device int32 [rows]
  *   workspace  device scratch, >= dt_argmax_rows_workspace_size bytes,
  *              256-byte aligned; may be NULL when that size is 0.
- * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_WORKSPACE, DT_ERR_HIP.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_UNSUPPORTED (rows > 65535),
+ * DT_ERR_WORKSPACE, DT_ERR_HIP.
  */
 int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t* out_idx,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dt_sample_rows_workspace_size -- bytes of device workspace dt_sample_rows
+ * needs (the same amount as dt_argmax_rows for the same shape).
+ */
+int dt_sample_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes);
+
+/*
+ * dt_sample_rows -- the target's sample at every node, T > 0 (GPU).
+ *
+ * Defined by: DARTree paper, Preliminaries > Speculative Sampling (exact
+ * target-sample matching, the DFlash rule: accept draft tokens while they
+ * equal the target's samples, emit the target's sample at the first mismatch;
+ * the target distribution at temperature T is p_T = softmax(logits / T)) and
+ * Experimental Setup > Evaluation Details (at T = 1 verification accepts the
+ * longest sampled prefix in the tree). Feeding out_idx to dt_accept_path in
+ * place of dt_argmax_rows' output gives that rule on a tree.
+ *
+ * The draw is Gumbel-max: out_idx[r] = the lowest j maximising
+ *   logits[r*row_stride + j] / T - ln(-ln U[r][j]),
+ * which is an exact sample of p_T. U comes from Philox4x32-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011):
+ *   w = Philox4x32-10(counter = (r, j / 4, offset & 0xffffffff, offset >> 32),
+ *                     key = (seed & 0xffffffff, seed >> 32))[j % 4]
+ *   U = (2 * (w >> 9) + 1) * 2^-24          (in (0, 1), exact in fp32)
+ * so every (seed, offset, row, j) has one fixed draw; use a new offset (or
+ * seed) per verification round. The comparison runs in fp32 as
+ * logits * (log2(e) / T) - log2(-log2 U), an order-preserving rescaling of the
+ * definition; candidates whose exact scores differ by less than fp32 rounding
+ * (a relative 1e-6 or so) may resolve either way.
+ *   logits, rows, vocab, row_stride, out_idx, workspace: as dt_argmax_rows.
+ *   temperature  > 0 and finite, with log2(e) / T representable in fp32
+ *                (T = 0, greedy decoding, is dt_argmax_rows); contract:
+ *                logits / T finite.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_VALUE (temperature),
+ * DT_ERR_UNSUPPORTED (rows > 65535), DT_ERR_WORKSPACE, DT_ERR_HIP.
+ */
+int dt_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, float temperature,
+                   uint64_t seed, uint64_t offset, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * dt_accept_path -- longest accepted root-to-leaf path and bonus token (GPU).

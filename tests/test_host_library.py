@@ -171,3 +171,18 @@ def test_argmax_and_walk_validation_errors():
     assert lib.dt_accept_path(1, bad.ctypes.data_as(_lib.P_i32), 4, 4, 4, 4, 4, 4, None) == _lib.DT_ERR_SHAPE
     big = np.array([0, 20000], np.int32)
     assert lib.dt_accept_path(1, big.ctypes.data_as(_lib.P_i32), 4, 4, 4, 4, 4, 4, None) == _lib.DT_ERR_UNSUPPORTED
+
+
+def test_sample_validation_errors():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.dt_sample_rows_workspace_size(-1, 10, ctypes.byref(n)) == _lib.DT_ERR_SHAPE
+    assert lib.dt_sample_rows_workspace_size(256, 151936, ctypes.byref(n)) in (_lib.DT_OK, _lib.DT_ERR_HIP)
+    for T in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert lib.dt_sample_rows(16, 4, 10, 10, T, 1, 2, 16, None, 0, None) == _lib.DT_ERR_VALUE, T
+    assert lib.dt_sample_rows(16, 4, 10, 9, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_SHAPE      # stride < vocab
+    assert lib.dt_sample_rows(16, 0, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_OK           # empty is a no-op
+    assert lib.dt_sample_rows(None, 2, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_NULL
+    assert lib.dt_sample_rows(16, 2, 10, 10, 1.0, 1, 2, None, None, 0, None) == _lib.DT_ERR_NULL
+    assert lib.dt_sample_rows(16, 70000, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_UNSUPPORTED
+    assert lib.dt_sample_rows(18, 2, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_SHAPE     # misaligned
