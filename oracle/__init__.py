@@ -24,6 +24,11 @@ What it computes, and where the pages define it:
 * ``walk``       -- the accepted root-to-leaf path and the bonus token (same
                     passage, plus the bonus-token sentence of Speculative
                     Sampling and the definition of tau in Experimental Setup).
+* ``commit``     -- the accepted path's keys and values copied into the KV
+                    cache rows that follow the verified prefix (Speculative
+                    Sampling: every round commits the accepted prefix and a
+                    bonus token; Figure 3: accepted tokens and features leave
+                    tree verification).
 * ``build_tree`` -- the DDTree best-first heap (DARTree paper, Figure 3
                     caption) and the top-mass optimum it reaches (Tree
                     Verification and DDTree, eq. 4 and the mass decomposition
@@ -34,4 +39,4 @@ something other than itself (library routines, closed forms, brute force,
 hand-worked fixtures under tests/golden/). No function is left unpinned.
 """
 
-from . import tree, attention, argmax, sample, walk, build_tree  # noqa: F401
+from . import tree, attention, argmax, sample, walk, commit, build_tree  # noqa: F401
