@@ -10,6 +10,7 @@ in libdtree (host C++ for the tree builder, HIP kernels for the rest).
     dt_argmax_rows      per-node greedy prediction (row arg-max, lowest index on ties)
     dt_sample_rows      per-node target sample at temperature T > 0 (Gumbel-max, Philox4x32-10)
     dt_accept_path      longest accepted root-to-leaf path and bonus token
+    dt_commit_kv        accepted path's keys and values into the KV cache, all layers
 """
 
 import ctypes
@@ -23,7 +24,7 @@ __all__ = [
     "DtError", "dt_status_string", "dt_abi_version", "dt_build_tree", "dt_validate_tree",
     "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention",
     "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_sample_rows_workspace_size", "dt_sample_rows",
-    "dt_accept_path", "library_path",
+    "dt_accept_path", "dt_commit_kv", "CommitArgs", "library_path",
 ]
 
 
@@ -274,3 +275,62 @@ def dt_accept_path(node_offsets, parent, token, argmax_idx, path=None, accept_le
                                     _stream(stream))
     _check(st, "dt_accept_path")
     return path, accept_len, bonus
+
+
+class CommitArgs:
+    """Marshalled arguments of dt_commit_kv, built once and reusable across
+    rounds (the pointer tables and host arrays stay alive with this object).
+
+    layout: AttnLayout (node offsets, prefix lengths before the commit, first
+    cache row per sequence); cache_rows: rows of room per sequence from its
+    first row; k_tree/v_tree/k_cache/v_cache: per-layer lists of bf16 CUDA
+    tensors ([N, Hkv, d] trees with unit head/dim strides, caches with any row
+    and head stride and unit dim stride, all layers alike); max_path: 0 or a
+    bound on accepted length + 1.
+    """
+
+    def __init__(self, layout, cache_rows, k_tree, v_tree, k_cache, v_cache, max_path=0):
+        L = len(k_tree)
+        if not (len(v_tree) == len(k_cache) == len(v_cache) == L) or L < 1:
+            raise ValueError("one tree K/V and cache K/V tensor per layer")
+        kt0, kc0 = k_tree[0], k_cache[0]
+        _, Hkv, d = kt0.shape
+        for t in list(k_tree) + list(v_tree):
+            if t.stride() != kt0.stride() or t.stride(2) != 1 or t.stride(1) != d:
+                raise ValueError("tree K/V: [rows][heads][d] with contiguous heads, all layers alike")
+        for t in list(k_cache) + list(v_cache):
+            if t.stride() != kc0.stride() or t.stride(2) != 1:
+                raise ValueError("cache K/V: d contiguous, all layers alike")
+        self.layout = layout
+        self.cache_rows = np.ascontiguousarray(cache_rows, dtype=np.int64)
+        if len(self.cache_rows) != layout.num_seqs:
+            raise ValueError("cache_rows needs one entry per sequence")
+        desc = _lib.dt_commit_desc()
+        desc.num_seqs = layout.num_seqs
+        desc.num_layers = L
+        desc.num_kv_heads = Hkv
+        desc.head_dim = d
+        desc.max_path = int(max_path)
+        desc.node_offsets = _ptr(layout.node_offsets, ctypes.c_int32)
+        desc.prefix_lens = _ptr(layout.prefix_lens, ctypes.c_int32)
+        desc.prefix_row_start = _ptr(layout.prefix_row_start, ctypes.c_int64)
+        desc.cache_rows = _ptr(self.cache_rows, ctypes.c_int64)
+        desc.tree_row_stride = kt0.stride(0)
+        desc.cache_row_stride = kc0.stride(0)
+        desc.cache_head_stride = kc0.stride(1)
+        self.desc = desc
+        arr = ctypes.c_void_p * L
+        self.k_tree = arr(*[t.data_ptr() for t in k_tree])
+        self.v_tree = arr(*[t.data_ptr() for t in v_tree])
+        self.k_cache = arr(*[t.data_ptr() for t in k_cache])
+        self.v_cache = arr(*[t.data_ptr() for t in v_cache])
+        self._keep = (k_tree, v_tree, k_cache, v_cache)
+
+
+def dt_commit_kv(args, path, accept_len, stream=None):
+    """Copy every layer's accepted-path K/V rows into the cache (GPU). ``args``:
+    CommitArgs; path int32 [N] and accept_len int32 [S] CUDA tensors as
+    dt_accept_path leaves them."""
+    st = _lib.load().dt_commit_kv(ctypes.byref(args.desc), args.k_tree, args.v_tree, args.k_cache, args.v_cache,
+                                  path.data_ptr(), accept_len.data_ptr(), _stream(stream))
+    _check(st, "dt_commit_kv")

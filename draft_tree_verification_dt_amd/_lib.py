@@ -50,6 +50,25 @@ class dt_attn_desc(ctypes.Structure):
     ]
 
 
+class dt_commit_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", c_i32),
+        ("num_layers", c_i32),
+        ("num_kv_heads", c_i32),
+        ("head_dim", c_i32),
+        ("max_path", c_i32),
+        ("node_offsets", P_i32),
+        ("prefix_lens", P_i32),
+        ("prefix_row_start", P_i64),
+        ("cache_rows", P_i64),
+        ("tree_row_stride", c_i64),
+        ("cache_row_stride", c_i64),
+        ("cache_head_stride", c_i64),
+    ]
+
+
+P_vp = ctypes.POINTER(ctypes.c_void_p)
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "dt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -64,6 +83,7 @@ SIGNATURES = {
     "dt_sample_rows": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, c_p,
                                       c_p, c_size, c_p]),
     "dt_accept_path": (ctypes.c_int, [c_i32, P_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "dt_commit_kv": (ctypes.c_int, [ctypes.POINTER(dt_commit_desc), P_vp, P_vp, P_vp, P_vp, c_p, c_p, c_p]),
 }
 
 _lib = None

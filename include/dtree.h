@@ -18,6 +18,7 @@
  *   dt_argmax_rows      GPU:  per-node greedy prediction (row arg-max)
  *   dt_sample_rows      GPU:  per-node target sample at temperature T > 0 (Gumbel-max)
  *   dt_accept_path      GPU:  longest accepted path and bonus token
+ *   dt_commit_kv        GPU:  accepted path's K/V into the KV cache, all layers
  *
  * Conventions shared by every entry point
  *  - Every function returns an int status: DT_OK (0) or a negative DT_ERR_*.
@@ -283,6 +284,61 @@ int dt_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
  */
 int dt_accept_path(int32_t num_seqs, const int32_t* node_offsets, const int32_t* parent, const int32_t* token,
                    const int32_t* argmax_idx, int32_t* path, int32_t* accept_len, int32_t* bonus, void* stream);
+
+/*
+ * Description of one KV commit. Counts and strides in elements (bf16).
+ *
+ * Sequence s has n_s = node_offsets[s+1] - node_offsets[s] tree nodes (>= 1),
+ * a verified prefix of P_s = prefix_lens[s] rows starting at cache row
+ * prefix_row_start[s], and cache_rows[s] rows of room from that start (the
+ * verified rows included). Host arrays are read during the call only.
+ */
+typedef struct dt_commit_desc {
+  int32_t num_seqs;                /* S >= 1 */
+  int32_t num_layers;              /* >= 1: one (tree K/V, cache K/V) quadruple per layer */
+  int32_t num_kv_heads;            /* Hkv >= 1 */
+  int32_t head_dim;                /* d >= 8, a multiple of 8 */
+  int32_t max_path;                /* 0, or a bound on accept_len[s] + 1 for every s (e.g. the
+                                      trees' depth + 1): fewer positions to launch and to reserve */
+  const int32_t* node_offsets;     /* host [S+1]; node_offsets[0] = 0, increasing */
+  const int32_t* prefix_lens;      /* host [S] */
+  const int64_t* prefix_row_start; /* host [S] */
+  const int64_t* cache_rows;       /* host [S]: must be >= P_s + min(n_s, max_path or n_s) */
+  int64_t tree_row_stride;         /* between node rows of k_tree/v_tree; 0 means Hkv*d */
+  int64_t cache_row_stride;        /* between cache rows (>= 8) */
+  int64_t cache_head_stride;       /* between KV heads within a cache row (>= d when Hkv > 1) */
+} dt_commit_desc;
+
+/*
+ * dt_commit_kv -- write the accepted path's keys and values into the KV cache (GPU).
+ *
+ * Defined by: DARTree paper, Preliminaries > Speculative Sampling (every round
+ * commits the accepted draft prefix followed by one bonus token) and Figure 3
+ * (tree verification passes the accepted tokens and their features on). The
+ * verification forward computed K/V for every tree node at position
+ * P_s + depth; for the accepted path path[0] = root, ..., path[L_s], where the
+ * node at path position t has depth t, the call copies, for every layer,
+ *   cache row prefix_row_start[s] + P_s + t  <-  tree row node_offsets[s] + path[t]
+ * for t = 0 .. L_s (K and V, all KV heads). Afterwards the sequence's verified
+ * prefix is P_s + L_s + 1 rows; the bonus token has no K/V yet (it is the next
+ * round's root). Only those rows are written.
+ *   k_tree, v_tree    host arrays [num_layers] of device pointers: [N][Hkv][d] bf16,
+ *                     row stride tree_row_stride (the same buffers dt_tree_attention read)
+ *   k_cache, v_cache  host arrays [num_layers] of device pointers: row r, head h
+ *                     at base + r*cache_row_stride + h*cache_head_stride
+ *   path, accept_len  device int32, as written by dt_accept_path ([N] tree-local
+ *                     nodes and [S] accepted lengths); read on the device, so
+ *                     the call needs no host synchronisation.
+ * Every buffer 16-byte aligned (path, accept_len: 4). Cache buffers must not
+ * alias tree buffers. Contract: path and accept_len as dt_accept_path leaves
+ * them; a path entry outside [0, n_s), or positions at or past max_path, are
+ * skipped, never written out of bounds.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE (counts, strides, alignment, room),
+ * DT_ERR_UNSUPPORTED (more than 65535 path positions), DT_ERR_HIP.
+ */
+int dt_commit_kv(const dt_commit_desc* desc, const void* const* k_tree, const void* const* v_tree,
+                 void* const* k_cache, void* const* v_cache, const int32_t* path, const int32_t* accept_len,
+                 void* stream);
 
 #ifdef __cplusplus
 }

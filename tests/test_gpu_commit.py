@@ -1,0 +1,183 @@
+"""GPU parity of dt_commit_kv against the oracle: bit-exact cache contents
+(every row, written or not) after committing the accepted paths that
+dt_accept_path leaves on the device, for ragged batches, several layers,
+row-major and head-major cache layouts, a max_path bound, the 36-layer B=256
+round, and a two-round chain where the second round attends over the
+committed cache."""
+
+import numpy as np
+import pytest
+
+import draft_tree_verification_dt_amd as dt
+from _helpers import assert_attention_close, dev_bf16, dev_i32, host_f64, require_gpu, tree
+from gen import rng as grng, tensors as gten
+from oracle import argmax as oarg, attention as oatt, commit as ocommit, walk as owalk
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+
+    return t.contiguous().view(torch.int16).cpu().numpy()
+
+
+def _planted_walk(r, nodes, vocab=64, shapes=("recursive", "deep", "chain"), plant_p=0.9):
+    parents, tokens, lgs = [], [], []
+    for s, n in enumerate(nodes):
+        p, t = tree(shapes[s % len(shapes)], n, int(r.integers(0, 1 << 30)), vocab=vocab)
+        lg = gten.logits(r, n, vocab)
+        gten.plant(r, lg, p, t, p=plant_p, pick="random")
+        parents.append(p)
+        tokens.append(t)
+        lgs.append(lg)
+    return parents, tokens, np.concatenate(lgs)
+
+
+def _run_commit(seed, nodes, plens, layers, Hkv, d, head_major=False, max_path=0, gap=5,
+                shapes=("recursive", "deep", "chain"), plant_p=0.9):
+    import torch
+
+    r = grng.stream(seed, "commit-gpu")
+    S = len(nodes)
+    offs = np.concatenate([[0], np.cumsum(nodes)]).astype(np.int32)
+    N = int(offs[-1])
+    room = [P + n + int(r.integers(0, 4)) for P, n in zip(plens, nodes)]
+    starts = np.concatenate([[gap], np.cumsum(np.array(room) + gap)[:-1] + gap]).astype(np.int64)
+    total = int(starts[-1] + room[-1] + gap)
+    parents, tokens, lg = _planted_walk(r, nodes, shapes=shapes, plant_p=plant_p)
+    am = dt.dt_argmax_rows(torch.from_numpy(lg).cuda())
+    path, acc, _ = dt.dt_accept_path(offs, dev_i32(np.concatenate(parents)), dev_i32(np.concatenate(tokens)), am)
+    kt = [dev_bf16(gten.normal_bf16(r, (N, Hkv, d))) for _ in range(layers)]
+    vt = [dev_bf16(gten.normal_bf16(r, (N, Hkv, d))) for _ in range(layers)]
+    host_kc = [gten.normal_bf16(r, (total, Hkv, d)) for _ in range(layers)]
+    host_vc = [gten.normal_bf16(r, (total, Hkv, d)) for _ in range(layers)]
+    if head_major:  # [Hkv][rows][d] storage viewed as [rows][Hkv][d]
+        kc = [dev_bf16(np.ascontiguousarray(x.transpose(1, 0, 2))).permute(1, 0, 2) for x in host_kc]
+        vc = [dev_bf16(np.ascontiguousarray(x.transpose(1, 0, 2))).permute(1, 0, 2) for x in host_vc]
+    else:
+        kc = [dev_bf16(x) for x in host_kc]
+        vc = [dev_bf16(x) for x in host_vc]
+    layout = dt.AttnLayout(offs, plens, starts)
+    args = dt.CommitArgs(layout, room, kt, vt, kc, vc, max_path=max_path)
+    print(f"commit seed={seed} nodes={nodes} layers={layers} Hkv={Hkv} d={d} head_major={head_major} "
+          f"max_path={max_path}", flush=True)
+    dt.dt_commit_kv(args, path, acc)
+    torch.cuda.synchronize()
+    path_h, acc_h = path.cpu().numpy(), acc.cpu().numpy()
+    want = owalk.batch_accept_path(np.concatenate(parents), np.concatenate(tokens), oarg.argmax_rows(lg), offs)
+    assert [L for _, L, _ in want] == list(acc_h)
+    acc_eff = acc_h if not max_path else np.minimum(acc_h, max_path - 1)
+    for l in range(layers):
+        wk, wv = ocommit.commit_kv(host_kc[l], host_vc[l], host_f64(kt[l]).astype(np.float32),
+                                   host_f64(vt[l]).astype(np.float32), path_h, acc_eff, offs, plens, starts)
+        np.testing.assert_array_equal(_bits(kc[l]), _bits(dev_bf16(wk)), err_msg=f"K layer {l}")
+        np.testing.assert_array_equal(_bits(vc[l]), _bits(dev_bf16(wv)), err_msg=f"V layer {l}")
+    return acc_h
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_commit_ragged_batches(seed):
+    require_gpu()
+    r = grng.stream(seed, "commit-shape")
+    S = int(r.integers(1, 6))
+    nodes = [int(r.integers(1, 120)) for _ in range(S)]
+    plens = [int(r.integers(0, 300)) for _ in range(S)]
+    acc = _run_commit(seed, nodes, plens, layers=3, Hkv=[1, 2, 8][seed], d=[64, 128, 128][seed])
+    assert acc.max() > 0
+
+
+def test_commit_head_major_cache():
+    require_gpu()
+    _run_commit(11, [40, 7, 90], [17, 0, 250], layers=2, Hkv=4, d=64, head_major=True)
+
+
+def test_commit_many_sequences_and_layers():
+    """More sequences and layers than one launch holds (32 and 40)."""
+    require_gpu()
+    r = grng.stream(12, "many")
+    nodes = [int(x) for x in r.integers(1, 30, size=37)]
+    plens = [int(x) for x in r.integers(0, 40, size=37)]
+    _run_commit(12, nodes, plens, layers=45, Hkv=2, d=16)
+
+
+def test_commit_max_path_bound():
+    """Positions at or past max_path are not written even when the accepted path is longer."""
+    require_gpu()
+    acc = _run_commit(13, [60, 60], [10, 10], layers=2, Hkv=2, d=32, max_path=3, shapes=("chain",), plant_p=1.0)
+    assert list(acc) == [59, 59]  # fully accepted chains: the bound cut 57 positions of each
+
+
+def test_commit_full_round_36_layers():
+    """The B=256 round's shape: 36 layers, Hkv 8, d 128, prefix 8192 with room
+    for the tree; the walk's path from a best-first tree and planted logits."""
+    import torch
+
+    require_gpu()
+    n, P, L, Hkv, d = 256, 8192, 36, 8, 128
+    r = grng.stream(14, "commit-full")
+    p, t = tree("heap", n, 14)
+    lg = gten.logits(r, n, 151936)
+    gten.plant(r, lg, p, t, p=0.8, pick="first")
+    am = dt.dt_argmax_rows(torch.from_numpy(lg).cuda())
+    offs = np.array([0, n], np.int32)
+    path, acc, _ = dt.dt_accept_path(offs, dev_i32(p), dev_i32(t), am)
+    kt = [gten.device_randn_bf16((n, Hkv, d), 14, "kt", l) for l in range(L)]
+    vt = [gten.device_randn_bf16((n, Hkv, d), 14, "vt", l) for l in range(L)]
+    kc = [gten.device_randn_bf16((P + n, Hkv, d), 14, "kc", l) for l in range(L)]
+    vc = [gten.device_randn_bf16((P + n, Hkv, d), 14, "vc", l) for l in range(L)]
+    before_k = [x.clone() for x in kc]
+    before_v = [x.clone() for x in vc]
+    args = dt.CommitArgs(dt.AttnLayout(offs, [P]), [P + n], kt, vt, kc, vc)
+    print("commit 36 layers B=256 P=8192", flush=True)
+    dt.dt_commit_kv(args, path, acc)
+    torch.cuda.synchronize()
+    Lh = int(acc.cpu()[0])
+    ph = path.cpu().numpy()
+    assert Lh > 0
+    idx = torch.from_numpy(ph[:Lh + 1].astype(np.int64)).cuda()
+    for l in range(L):
+        assert torch.equal(kc[l][P:P + Lh + 1], kt[l][idx]) and torch.equal(vc[l][P:P + Lh + 1], vt[l][idx]), l
+        assert torch.equal(kc[l][:P], before_k[l][:P]) and torch.equal(kc[l][P + Lh + 1:], before_k[l][P + Lh + 1:])
+        assert torch.equal(vc[l][:P], before_v[l][:P]) and torch.equal(vc[l][P + Lh + 1:], before_v[l][P + Lh + 1:])
+
+
+def test_two_rounds_attend_over_the_committed_cache():
+    """Round 1: attention, argmax, walk, commit. Round 2: a new tree attends over
+    the P + L + 1 committed rows; its output matches the oracle evaluated on the
+    oracle-committed cache."""
+    import torch
+
+    require_gpu()
+    r = grng.stream(15, "two-rounds")
+    Hq, Hkv, d, P, vocab = 8, 2, 128, 300, 64
+    n1, n2 = 50, 40
+    p1, t1 = tree("recursive", n1, 151, vocab=vocab)
+    p2, _ = tree("deep", n2, 152, vocab=vocab)
+    ops1 = gten.attention_operands(r, n1, P, Hq, Hkv, d)
+    room = P + n1
+    kc_h = np.zeros((room, Hkv, d), np.float32)
+    vc_h = np.zeros((room, Hkv, d), np.float32)
+    kc_h[:P], vc_h[:P] = ops1["k_prefix"], ops1["v_prefix"]
+    kc, vc = dev_bf16(kc_h), dev_bf16(vc_h)
+    kt1, vt1 = dev_bf16(ops1["k_tree"]), dev_bf16(ops1["v_tree"])
+    lg = gten.logits(r, n1, vocab)
+    gten.plant(r, lg, p1, t1, p=0.95, pick="random")
+    offs1 = np.array([0, n1], np.int32)
+    lay1 = dt.AttnLayout(offs1, [P], [0])
+    dt.dt_tree_attention(dev_bf16(ops1["q"]), kt1, vt1, kc, vc, dev_i32(p1), lay1)
+    am = dt.dt_argmax_rows(torch.from_numpy(lg).cuda())
+    path, acc, _ = dt.dt_accept_path(offs1, dev_i32(p1), dev_i32(t1), am)
+    dt.dt_commit_kv(dt.CommitArgs(lay1, [room], [kt1], [vt1], [kc], [vc]), path, acc)
+    torch.cuda.synchronize()
+    L1 = int(acc.cpu()[0])
+    P2 = P + L1 + 1
+    wk, wv = ocommit.commit_kv(kc_h, vc_h, ops1["k_tree"], ops1["v_tree"], path.cpu().numpy(), [L1], offs1, [P], [0])
+    ops2 = gten.attention_operands(r, n2, 0, Hq, Hkv, d)
+    print(f"two rounds: L1={L1} P2={P2}", flush=True)
+    out2 = dt.dt_tree_attention(dev_bf16(ops2["q"]), dev_bf16(ops2["k_tree"]), dev_bf16(ops2["v_tree"]), kc, vc,
+                                dev_i32(p2), dt.AttnLayout([0, n2], [P2], [0]))
+    torch.cuda.synchronize()
+    ref = oatt.tree_attention(ops2["q"], ops2["k_tree"], ops2["v_tree"], wk[:P2], wv[:P2], p2)
+    assert_attention_close(host_f64(out2), ref, what="round 2")
+    assert L1 > 0

@@ -186,3 +186,50 @@ def test_sample_validation_errors():
     assert lib.dt_sample_rows(16, 2, 10, 10, 1.0, 1, 2, None, None, 0, None) == _lib.DT_ERR_NULL
     assert lib.dt_sample_rows(16, 70000, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_UNSUPPORTED
     assert lib.dt_sample_rows(18, 2, 10, 10, 1.0, 1, 2, 16, None, 0, None) == _lib.DT_ERR_SHAPE     # misaligned
+
+
+def _commit_desc(**kw):
+    offs = np.array(kw.pop("offs", [0, 4, 9]), np.int32)
+    S = len(offs) - 1
+    plens = np.array(kw.pop("plens", [10] * S), np.int32)
+    starts = np.array(kw.pop("starts", [0, 100][:S]), np.int64)
+    rows = np.array(kw.pop("rows", [100] * S), np.int64)
+    d = _lib.dt_commit_desc()
+    d.num_seqs, d.num_layers, d.num_kv_heads, d.head_dim, d.max_path = S, 2, 8, 128, 0
+    d.node_offsets = offs.ctypes.data_as(_lib.P_i32)
+    d.prefix_lens = plens.ctypes.data_as(_lib.P_i32)
+    d.prefix_row_start = starts.ctypes.data_as(_lib.P_i64)
+    d.cache_rows = rows.ctypes.data_as(_lib.P_i64)
+    d.tree_row_stride, d.cache_row_stride, d.cache_head_stride = 0, 1024, 128
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d, (offs, plens, starts, rows)
+
+
+def test_commit_validation_errors():
+    lib = _lib.load()
+    ptrs = lambda *v: (ctypes.c_void_p * 2)(*v)  # noqa: E731
+    good = ptrs(256, 512)
+    cases = [
+        (dict(num_seqs=0), _lib.DT_ERR_SHAPE), (dict(num_layers=0), _lib.DT_ERR_SHAPE),
+        (dict(head_dim=12), _lib.DT_ERR_SHAPE), (dict(max_path=-1), _lib.DT_ERR_SHAPE),
+        (dict(tree_row_stride=100), _lib.DT_ERR_SHAPE), (dict(cache_row_stride=1020), _lib.DT_ERR_SHAPE),
+        (dict(cache_head_stride=64), _lib.DT_ERR_SHAPE),
+        (dict(offs=[1, 4, 9]), _lib.DT_ERR_SHAPE), (dict(offs=[0, 4, 4]), _lib.DT_ERR_SHAPE),
+        (dict(plens=[10, -1]), _lib.DT_ERR_SHAPE),
+        (dict(rows=[13, 100]), _lib.DT_ERR_SHAPE),                 # 10 + 4 nodes do not fit in 13 rows
+        (dict(rows=[13, 100], max_path=3), _lib.DT_OK),            # ... but a 3-position path does
+    ]
+    for kw, code in cases:
+        d, keep = _commit_desc(**kw)
+        if code == _lib.DT_OK:
+            # the description is valid: validation reaches the device buffers (checked last) and stops there
+            assert lib.dt_commit_kv(ctypes.byref(d), good, ptrs(256, 0), good, good, 16, 16, None) == _lib.DT_ERR_NULL
+            continue
+        assert lib.dt_commit_kv(ctypes.byref(d), good, good, good, good, 16, 16, None) == code, kw
+    d, keep = _commit_desc()
+    assert lib.dt_commit_kv(None, good, good, good, good, 16, 16, None) == _lib.DT_ERR_NULL
+    assert lib.dt_commit_kv(ctypes.byref(d), None, good, good, good, 16, 16, None) == _lib.DT_ERR_NULL
+    assert lib.dt_commit_kv(ctypes.byref(d), ptrs(256, 0), good, good, good, 16, 16, None) == _lib.DT_ERR_NULL
+    assert lib.dt_commit_kv(ctypes.byref(d), ptrs(256, 520), good, good, good, 16, 16, None) == _lib.DT_ERR_SHAPE
+    assert lib.dt_commit_kv(ctypes.byref(d), good, good, good, good, 18, 16, None) == _lib.DT_ERR_SHAPE
