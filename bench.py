@@ -5,9 +5,13 @@ A step runs the whole verification path over one synthetic round:
   2. upload parent/token (pinned host -> HBM, async)
   3. dt_tree_attention  x L layers, each with its own KV cache
   4. dt_argmax_rows     greedy prediction at every node over the full vocabulary
+                        (dt_sample_rows instead with --temperature T > 0)
   5. dt_accept_path     accepted path, length and bonus token
+  6. dt_commit_kv       only with --commit: the accepted rows into every layer's cache
 Inputs (KV caches, Q/K/V of the tree, logits) are resident in HBM before the
-timed region; only the tree itself is built per step, as a round would.
+timed region; only the tree itself is built per step, as a round would. After
+the timed steps the T = 1 target-sampling kernel and the KV commit are timed on
+their own as well (fields "sample" and "commit").
 
 Default workload: Qwen3-4B-shaped target (32 query heads, 8 KV heads, head dim
 128, 36 layers, vocabulary 151936), one sequence with an 8192-token verified
@@ -39,7 +43,9 @@ def parse():
     ap.add_argument("--workload", default="round", help="gen.configs name (round, b128, b256, chain16, ragged, long)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="0: greedy verification (dt_argmax_rows); > 0: exact target-sample matching (dt_sample_rows)")
+    ap.add_argument("--commit", action="store_true", help="commit the accepted K/V rows in every step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
@@ -49,7 +55,7 @@ def parse():
 class Round:
     """Device-resident inputs of one workload and the launches of one step."""
 
-    def __init__(self, w, device):
+    def __init__(self, w, device, temperature=0.0, commit=False):
         import torch
 
         import draft_tree_verification_dt_amd as dt
@@ -57,14 +63,17 @@ class Round:
 
         self.w, self.dt, self.torch = w, dt, torch
         self.dev = device
+        self.temperature, self.do_commit = float(temperature), bool(commit)
         S, Hq, Hkv, d, L = w.num_seqs, w.Hq, w.Hkv, w.d, w.layers
-        N, PT = w.total_nodes, w.total_prefix
+        N, CR = w.total_nodes, w.total_cache_rows
         sc = 1.0 / np.sqrt(d)
         self.offs = w.node_offsets()
-        self.layout = dt.AttnLayout(self.offs, w.prefix_lens, w.prefix_row_starts())
+        # each sequence's cache keeps room for its tree after the prefix (rows a commit writes)
+        self.starts = w.cache_row_starts()
+        self.layout = dt.AttnLayout(self.offs, w.prefix_lens, self.starts)
         # per-layer operands; every layer has its own KV cache
-        self.kp = [gten.device_randn_bf16((PT, Hkv, d), w.seed, "kp", l, scale=sc) for l in range(L)]
-        self.vp = [gten.device_randn_bf16((PT, Hkv, d), w.seed, "vp", l, scale=sc) for l in range(L)]
+        self.kp = [gten.device_randn_bf16((CR, Hkv, d), w.seed, "kp", l, scale=sc) for l in range(L)]
+        self.vp = [gten.device_randn_bf16((CR, Hkv, d), w.seed, "vp", l, scale=sc) for l in range(L)]
         self.q = [gten.device_randn_bf16((N, Hq, d), w.seed, "q", l, scale=sc) for l in range(L)]
         self.kt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "kt", l, scale=sc) for l in range(L)]
         self.vt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "vt", l, scale=sc) for l in range(L)]
@@ -100,6 +109,9 @@ class Round:
         ws_am = dt.dt_argmax_rows_workspace_size(N, w.vocab)
         self.ws_am = torch.empty(max(ws_am, 256), dtype=torch.uint8, device=device)
         self.upload_done = [None, None]
+        self.commit_args = dt.CommitArgs(self.layout, np.asarray(w.prefix_lens) + np.asarray(w.nodes), self.kt,
+                                         self.vt, self.kp, self.vp, max_path=w.depths + 1)
+        self.sample_seed = 0x5EED_0000 + w.seed
         self._prepare_raw_calls()
         self.step_idx = 0
 
@@ -155,16 +167,38 @@ class Round:
         if events is not None:
             events[1].record()
         lg = self.logits[t]
-        st = self.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), self.am.data_ptr(),
-                                     self.ws_am.data_ptr(), self.ws_am.numel(), self.stream)
-        if st != 0:
-            raise self.dt.DtError(st, "dt_argmax_rows")
+        if self.temperature > 0:
+            self.sample(lg, self.step_idx)
+        else:
+            st = self.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), self.am.data_ptr(),
+                                         self.ws_am.data_ptr(), self.ws_am.numel(), self.stream)
+            if st != 0:
+                raise self.dt.DtError(st, "dt_argmax_rows")
         st = self.lib.dt_accept_path(self.w.num_seqs, self.offs_ptr, self.d_tree[0].data_ptr(),
                                      self.d_tree[1].data_ptr(), self.am.data_ptr(), self.path.data_ptr(),
                                      self.acc.data_ptr(), self.bonus.data_ptr(), self.stream)
         if st != 0:
             raise self.dt.DtError(st, "dt_accept_path")
+        if self.do_commit:
+            self.commit()
         self.step_idx += 1
+
+    def sample(self, lg, offset, temperature=None):
+        """Target samples of every node into self.am (the round's offset keys the draws)."""
+        T = self.temperature if temperature is None else temperature
+        st = self.lib.dt_sample_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), T, self.sample_seed,
+                                     offset, self.am.data_ptr(), self.ws_am.data_ptr(), self.ws_am.numel(), self.stream)
+        if st != 0:
+            raise self.dt.DtError(st, "dt_sample_rows")
+
+    def commit(self):
+        import ctypes
+
+        a = self.commit_args
+        st = self.lib.dt_commit_kv(ctypes.byref(a.desc), a.k_tree, a.v_tree, a.k_cache, a.v_cache,
+                                   self.path.data_ptr(), self.acc.data_ptr(), self.stream)
+        if st != 0:
+            raise self.dt.DtError(st, "dt_commit_kv")
 
     def attention_flops(self, table):
         """Algorithmic flops of one layer for the trees of `table` (ancestor pairs only)."""
@@ -218,55 +252,80 @@ def tree_shape(rnd):
             "tables": len(rnd.trees)}
 
 
-def time_argmax_calls(rnd, reps):
+def time_on_stream(rnd, fn, reps):
+    """Mean GPU time of fn() in ms, from HIP events recorded around it on the
+    library's stream. Two attention calls are queued ahead of each start event,
+    so the host has enqueued the events and fn's kernels before the GPU reaches
+    them: the interval is GPU execution, not host launch latency. One untimed
+    call comes first."""
     torch = rnd.torch
+    fn(0)  # the first launch of a kernel also loads its code object
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i in range(reps):
-        lg = rnd.logits[i % N_TABLES]
+        rnd.attention(0)
+        rnd.attention(1 % rnd.w.layers)
         evs[i][0].record()
-        rnd.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), rnd.am.data_ptr(),
-                               rnd.ws_am.data_ptr(), rnd.ws_am.numel(), rnd.stream)
+        fn(i)
         evs[i][1].record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def parity_check(rnd):
-    """Re-check the timed path against the oracle: sampled attention rows of
-    layer 0 and the whole argmax / walk of the last step's table."""
-    from oracle import argmax as oarg, attention as oatt, walk as owalk
+def time_argmax_calls(rnd, reps):
+    def call(i):
+        lg = rnd.logits[i % N_TABLES]
+        st = rnd.lib.dt_argmax_rows(lg.data_ptr(), lg.shape[0], lg.shape[1], lg.stride(0), rnd.am.data_ptr(),
+                                    rnd.ws_am.data_ptr(), rnd.ws_am.numel(), rnd.stream)
+        if st != 0:
+            raise rnd.dt.DtError(st, "dt_argmax_rows")
 
-    torch, w = rnd.torch, rnd.w
+    return time_on_stream(rnd, call, reps)
+
+
+def time_sample_calls(rnd, reps, temperature=1.0):
+    return time_on_stream(rnd, lambda i: rnd.sample(rnd.logits[i % N_TABLES], 1000 + i, temperature), reps)
+
+
+def time_commit_calls(rnd, reps):
+    """dt_commit_kv over every layer for the accepted paths the last step left on the device."""
+    ms = time_on_stream(rnd, lambda i: rnd.commit(), reps)
+    acc = rnd.acc.cpu().numpy()
+    w = rnd.w
+    moved = int(2 * 2 * (acc + 1).sum() * w.Hkv * w.d * 2 * w.layers)  # read + write of K and V rows
+    return ms, moved, acc
+
+
+def reference_outputs(rnd, t1_offset):
+    """One more (untimed) round on candidate table 0 whose outputs the CPU
+    baseline leg checks: every layer's attention, the greedy tokens, the walk,
+    the T = 1 samples of the same logits, and the commit of the accepted rows."""
+    torch = rnd.torch
+    rnd.step_idx = (rnd.step_idx // N_TABLES + 1) * N_TABLES  # next step uses table 0
+    saved = rnd.temperature, rnd.do_commit
+    rnd.temperature, rnd.do_commit = 0.0, False
+    rnd.step()
+    rnd.temperature, rnd.do_commit = saved
     torch.cuda.synchronize()
-    t = (rnd.step_idx - 1) % N_TABLES
-    f = lambda x: x.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    rng = np.random.default_rng(0)
-    worst = 0.0
-    for s in range(w.num_seqs):
-        a, b = int(rnd.offs[s]), int(rnd.offs[s + 1])
-        p0, P = int(w.prefix_row_starts()[s]), w.prefix_lens[s]
-        parent = rnd.trees[t][s][0]
-        rows = [(int(rng.integers(0, b - a)), int(rng.integers(0, w.Hq))) for _ in range(16)]
-        ref = oatt.tree_attention_rows(f(rnd.q[0][a:b]), f(rnd.kt[0][a:b]), f(rnd.vt[0][a:b]), f(rnd.kp[0][p0:p0 + P]),
-                                       f(rnd.vp[0][p0:p0 + P]), parent, rows)
-        got = np.stack([f(rnd.out[0][a + i, h]) for i, h in rows])
-        err = np.abs(got - ref).max(-1) / np.abs(ref).max(-1)
-        worst = max(worst, float(err.max()))
-    am_ref = oarg.argmax_rows(rnd.logits[t].cpu().numpy())
-    am_ok = bool(np.array_equal(rnd.am.cpu().numpy(), am_ref))
-    walks = owalk.batch_accept_path(np.concatenate([x[0] for x in rnd.trees[t]]),
-                                    np.concatenate([x[1] for x in rnd.trees[t]]), am_ref, rnd.offs)
-    acc, bon = rnd.acc.cpu().numpy(), rnd.bonus.cpu().numpy()
-    walk_ok = all(int(acc[s]) == L and int(bon[s]) == bo for s, (_, L, bo) in enumerate(walks))
-    return {"attention_row_rel_err_max": worst, "argmax_exact": am_ok, "walk_exact": walk_ok,
-            "mean_accept_len": float(np.mean([L for _, L, _ in walks]))}
+    ref = {"am": rnd.am.cpu().numpy(), "acc": rnd.acc.cpu().numpy(), "bonus": rnd.bonus.cpu().numpy(),
+           "path": rnd.path.cpu().numpy()}
+    rnd.sample(rnd.logits[0], t1_offset, 1.0)
+    torch.cuda.synchronize()
+    ref["t1"] = rnd.am.cpu().numpy()
+    before = (rnd.kp[0].clone(), rnd.vp[0].clone())
+    rnd.commit()
+    torch.cuda.synchronize()
+    ref["commit_layer0"] = (before, (rnd.kp[0], rnd.vp[0]))
+    return ref
 
 
-def cpu_baseline(rnd, budget_s):
+def cpu_baseline(rnd, budget_s, ref, t1_offset):
     """The oracle, as it is, on this host's cores: a bounded sample of the same
     round (some of the layers' attention, plus argmax, walk and tree build),
-    scaled to a full round."""
-    from oracle import argmax as oarg, attention as oatt, build_tree as obt, walk as owalk
+    scaled to a full round. Its outputs are compared with the GPU's outputs of
+    the same round (`ref`), which gives the parity record."""
+    from oracle import argmax as oarg, attention as oatt, build_tree as obt, commit as ocommit, sample as osmp
+    from oracle import walk as owalk
 
     w, torch = rnd.w, rnd.torch
     try:
@@ -281,16 +340,21 @@ def cpu_baseline(rnd, budget_s):
     t0 = time.perf_counter()
     trees = [obt.build_tree_heap(lp, tok, root, n) for lp, tok, root, n in rnd.tables[t]]
     t_build = time.perf_counter() - t0
+    build_ok = all(list(a[0]) == list(b[0]) and list(a[1]) == list(b[1]) for a, b in zip(trees, rnd.trees[t]))
     parents = [np.array(x[0]) for x in trees]
-    starts = w.prefix_row_starts()
     layer_times = []
     spent = 0.0
+    worst_abs, worst_rel = 0.0, 0.0
     for l in range(w.layers):
         args = [f(x[l]) for x in (rnd.q, rnd.kt, rnd.vt, rnd.kp, rnd.vp)]
         t0 = time.perf_counter()
-        oatt.batch_tree_attention(*args, np.concatenate(parents), rnd.offs, w.prefix_lens, starts)
+        o = oatt.batch_tree_attention(*args, np.concatenate(parents), rnd.offs, w.prefix_lens, rnd.starts)
         layer_times.append(time.perf_counter() - t0)
         spent += layer_times[-1]
+        got = rnd.out[l].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - o)
+        worst_abs = max(worst_abs, float(err.max()))
+        worst_rel = max(worst_rel, float((err.max(-1) / np.maximum(np.abs(o).max(-1), 1e-30)).max()))
         if spent > budget_s and len(layer_times) >= 1:
             break
     lg = rnd.logits[t].cpu().numpy()
@@ -298,18 +362,45 @@ def cpu_baseline(rnd, budget_s):
     am = oarg.argmax_rows(lg)
     t_arg = time.perf_counter() - t0
     t0 = time.perf_counter()
-    owalk.batch_accept_path(np.concatenate(parents), np.concatenate([x[1] for x in trees]), am, rnd.offs)
+    walks = owalk.batch_accept_path(np.concatenate(parents), np.concatenate([x[1] for x in trees]), am, rnd.offs)
     t_walk = time.perf_counter() - t0
+    walk_ok = all(int(ref["acc"][s]) == L and int(ref["bonus"][s]) == bo and
+                  list(ref["path"][rnd.offs[s]:rnd.offs[s] + L + 1]) == pth for s, (pth, L, bo) in enumerate(walks))
+    # T = 1: the oracle's Gumbel-max over the same logits and stream; a mismatch must be a near tie in fp32
+    ids = np.unique(np.linspace(0, lg.shape[0] - 1, min(lg.shape[0], 256)).astype(np.int64))
+    t0 = time.perf_counter()
+    scores = np.concatenate([osmp.perturbed_scores(lg[ids[i:i + 32]], 1.0, ids[i:i + 32], rnd.sample_seed, t1_offset)
+                             for i in range(0, len(ids), 32)])
+    smp = np.argmax(scores, axis=1)
+    t_smp = time.perf_counter() - t0
+    gpu = ref["t1"][ids].astype(np.int64)
+    rows = np.arange(len(ids))
+    gap = scores[rows, smp] - scores[rows, gpu]
+    tol = 2 * 2.0 ** -22 * (np.abs(lg[ids]).max(axis=1) * 1.4426950408889634 + 24.0) / 1.4426950408889634
+    sample_ok = bool(((gpu == smp) | (gap <= tol)).all())
+    # commit: layer 0's cache after the GPU commit equals the oracle's commit of the cache before it
+    (k0, v0), (k1, v1) = ref["commit_layer0"]
+    wk, wv = ocommit.commit_kv(f(k0), f(v0), f(rnd.kt[0]), f(rnd.vt[0]), ref["path"], ref["acc"], rnd.offs,
+                               w.prefix_lens, rnd.starts)
+    commit_ok = bool(np.array_equal(wk, f(k1)) and np.array_equal(wv, f(v1)))
     round_s = t_build + np.mean(layer_times) * w.layers + t_arg + t_walk
     flops = rnd.attention_flops(t) * w.layers
+    parity = {"layers_checked": len(layer_times), "attention_max_abs_err": worst_abs,
+              "attention_row_rel_err_max": worst_rel,
+              "attention_ok": bool(worst_abs <= 2e-2 and worst_rel <= 1e-2), "build_tree_exact": bool(build_ok),
+              "argmax_exact": bool(np.array_equal(ref["am"], am)), "walk_exact": bool(walk_ok),
+              "sample_t1_ok": sample_ok, "sample_t1_rows_checked": int(len(ids)),
+              "sample_t1_exact_rows": int((gpu == smp).sum()),
+              "commit_exact": commit_ok, "mean_accept_len": float(np.mean([L for _, L, _ in walks]))}
     return {
         "value": flops / round_s / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas_threads) if blas_threads else cores),
         "kind": "oracle",
         "sample": f"{len(layer_times)} of {w.layers} layers' attention timed (numpy float64, dense ancestor mask), "
                   f"plus tree build, argmax and walk once; scaled to one full round",
         "us_per_round": round_s * 1e6, "host_cores_visible": cores, "blas_threads": blas_threads,
-        "seconds": {"build": t_build, "attention_per_layer": float(np.mean(layer_times)), "argmax": t_arg, "walk": t_walk},
-    }
+        "seconds": {"build": t_build, "attention_per_layer": float(np.mean(layer_times)), "argmax": t_arg,
+                    "walk": t_walk, "sample_t1": t_smp},
+    }, parity
 
 
 def main():
@@ -336,7 +427,7 @@ def main():
         print(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr, flush=True)
         del src_buf, dst_buf
     w = gconf.get(args.workload)
-    rnd = Round(w, dev)
+    rnd = Round(w, dev, temperature=args.temperature, commit=args.commit)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -357,9 +448,10 @@ def main():
     round_flops = flops_layer * w.layers
     value = round_flops / (ms_per_step / 1e3) / 1e12
 
-    parity = None if args.no_parity else parity_check(rnd)  # checks the last timed step's outputs
     att_mean_ms = float(np.mean(att_call_ms))
     arg_ms = time_argmax_calls(rnd, reps=10)
+    smp_ms = time_sample_calls(rnd, reps=10)
+    com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
@@ -382,11 +474,19 @@ def main():
                      "traffic_source": traffic["source"] if traffic else None},
         "argmax": {"ms": arg_ms, "GB/s": argmax_bytes / (arg_ms / 1e3) / 1e9,
                    "frac_hbm": argmax_bytes / (arg_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "parity": parity,
+        "sample": {"kernel": "dt_sample_rows (Gumbel-max, Philox4x32-10), T = 1", "ms": smp_ms,
+                   "GB/s": argmax_bytes / (smp_ms / 1e3) / 1e9,
+                   "frac_hbm": argmax_bytes / (smp_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "commit": {"kernel": "dt_commit_kv, all layers in one call", "us": com_ms * 1e3, "bytes": com_bytes,
+                   "GB/s": com_bytes / (com_ms / 1e3) / 1e9, "accept_len": com_acc.tolist()},
+        "step_variant": {"temperature": args.temperature, "commit": bool(args.commit)},
+        "parity": None,
         "trees": tree_shape(rnd),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(rnd, args.cpu_budget_s)
+        t1_offset = 424242
+        ref = reference_outputs(rnd, t1_offset)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(rnd, args.cpu_budget_s, ref, t1_offset)
     print(json.dumps(rec), flush=True)
 
 

@@ -56,6 +56,16 @@ class Workload:
     def prefix_row_starts(self):
         return np.concatenate([[0], np.cumsum(self.prefix_lens)[:-1]]).astype(np.int64)
 
+    def cache_row_starts(self):
+        """First cache row of every sequence when each keeps room for its tree
+        after its prefix (P_s + n_s rows), so that accepted rows can be committed."""
+        room = np.asarray(self.prefix_lens, np.int64) + np.asarray(self.nodes, np.int64)
+        return np.concatenate([[0], np.cumsum(room)[:-1]]).astype(np.int64)
+
+    @property
+    def total_cache_rows(self):
+        return int(sum(self.prefix_lens) + sum(self.nodes))
+
     @property
     def total_nodes(self):
         return int(sum(self.nodes))
