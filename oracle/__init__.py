@@ -29,6 +29,10 @@ What it computes, and where the pages define it:
                     Sampling: every round commits the accepted prefix and a
                     bonus token; Figure 3: accepted tokens and features leave
                     tree verification).
+* ``dartree``    -- DARTree's construction: per-depth top-K candidates with
+                    log-softmax values, depth-wise fixed-width expansion scored
+                    by eq. 5 (Algorithm 1), and deferred top-B pruning with the
+                    best-first heap it equals (eq. 6, Lemma 1, Appendix C).
 * ``build_tree`` -- the DDTree best-first heap (DARTree paper, Figure 3
                     caption) and the top-mass optimum it reaches (Tree
                     Verification and DDTree, eq. 4 and the mass decomposition
@@ -39,4 +43,4 @@ something other than itself (library routines, closed forms, brute force,
 hand-worked fixtures under tests/golden/). No function is left unpinned.
 """
 
-from . import tree, attention, argmax, sample, walk, commit, build_tree  # noqa: F401
+from . import tree, attention, argmax, sample, walk, commit, build_tree, dartree  # noqa: F401
