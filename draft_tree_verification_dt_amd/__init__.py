@@ -11,6 +11,9 @@ in libdtree (host C++ for the tree builder, HIP kernels for the rest).
     dt_sample_rows      per-node target sample at temperature T > 0 (Gumbel-max, Philox4x32-10)
     dt_accept_path      longest accepted root-to-leaf path and bonus token
     dt_commit_kv        accepted path's keys and values into the KV cache, all layers
+    dt_topk_rows        per-depth top-K draft candidates with log-softmax values
+    dt_expand_depth     one depth of DARTree's fixed-width supertree
+    dt_prune_topb       deferred top-B pruning of the supertree into the verification tree
 """
 
 import ctypes
@@ -24,7 +27,8 @@ __all__ = [
     "DtError", "dt_status_string", "dt_abi_version", "dt_build_tree", "dt_validate_tree",
     "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention",
     "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_sample_rows_workspace_size", "dt_sample_rows",
-    "dt_accept_path", "dt_commit_kv", "CommitArgs", "library_path",
+    "dt_accept_path", "dt_commit_kv", "CommitArgs", "dt_topk_rows_workspace_size", "dt_topk_rows",
+    "dt_expand_depth", "dt_prune_topb", "library_path",
 ]
 
 
@@ -334,3 +338,88 @@ def dt_commit_kv(args, path, accept_len, stream=None):
     st = _lib.load().dt_commit_kv(ctypes.byref(args.desc), args.k_tree, args.v_tree, args.k_cache, args.v_cache,
                                   path.data_ptr(), accept_len.data_ptr(), _stream(stream))
     _check(st, "dt_commit_kv")
+
+
+def dt_topk_rows_workspace_size(rows, vocab, k):
+    n = ctypes.c_size_t(0)
+    _check(_lib.load().dt_topk_rows_workspace_size(int(rows), int(vocab), int(k), ctypes.byref(n)),
+           "dt_topk_rows_workspace_size")
+    return n.value
+
+
+def dt_topk_rows(logits, k, out_token=None, out_logprob=None, workspace=None, stream=None):
+    """The k best entries of every row of a [rows, vocab] float32 CUDA tensor
+    (unit column stride), ordered by (logit desc, index asc), with their
+    log-softmax values. Returns (tokens int32 [rows, k], logprob float32 [rows, k])."""
+    import torch
+
+    rows, vocab = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits: vocab dimension must be contiguous")
+    dev = logits.device
+    if out_token is None:
+        out_token = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if out_logprob is None:
+        out_logprob = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    for t in (out_token, out_logprob):
+        if not t.is_contiguous() or tuple(t.shape) != (rows, k):
+            raise ValueError("outputs must be contiguous [rows, k]")
+    if workspace is None:
+        workspace = torch.empty(max(dt_topk_rows_workspace_size(rows, vocab, k), 256), dtype=torch.uint8, device=dev)
+    st = _lib.load().dt_topk_rows(logits.data_ptr(), rows, vocab, logits.stride(0), int(k), out_token.data_ptr(),
+                                  out_logprob.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "dt_topk_rows")
+    return out_token, out_logprob
+
+
+def dt_expand_depth(parent_score, child_logq, cand_token, w, beta, out=None, stream=None):
+    """One depth of the fixed-width supertree (GPU). parent_score float32 [S, w_prev]
+    (any row stride), child_logq float32 [S, w_prev, k] (each sequence's block
+    contiguous), cand_token int32 [S, k] (any row stride). ``out``: optional
+    (sel_parent, sel_cand, sel_token, sel_score) of shape [S, w] sharing one row
+    stride (e.g. views of a [S, depths, w] supertree). Returns that tuple."""
+    import torch
+
+    S, w_prev, k = child_logq.shape
+    if child_logq.stride(2) != 1 or child_logq.stride(1) != k:
+        raise ValueError("child_logq: each sequence's [w_prev, k] block must be contiguous")
+    for t in (parent_score, cand_token):
+        if t.stride(1) != 1:
+            raise ValueError("parent_score / cand_token rows must be contiguous")
+    dev = child_logq.device
+    if out is None:
+        out = (torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.int32, device=dev),
+               torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.float32, device=dev))
+    rs = out[0].stride(0)
+    if any(t.stride(0) != rs or t.stride(1) != 1 for t in out):
+        raise ValueError("outputs must share one row stride with contiguous rows")
+    st = _lib.load().dt_expand_depth(S, w_prev, k, int(w), float(beta), parent_score.data_ptr(), parent_score.stride(0),
+                                     child_logq.data_ptr(), child_logq.stride(0), cand_token.data_ptr(),
+                                     cand_token.stride(0), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                     out[3].data_ptr(), rs, _stream(stream))
+    _check(st, "dt_expand_depth")
+    return out
+
+
+def dt_prune_topb(sel_parent, sel_token, sel_score, root_token, budget, out=None, stream=None):
+    """Deferred top-B pruning (GPU). sel_* [S, depths, w] contiguous (dt_expand_depth's
+    per-depth outputs stacked), root_token int32 [S]. Returns (parent, token, depth,
+    score) [S, budget + 1] and n_out [S]."""
+    import torch
+
+    S, depths, w = sel_parent.shape
+    for t in (sel_parent, sel_token, sel_score):
+        if not t.is_contiguous() or tuple(t.shape) != (S, depths, w):
+            raise ValueError("supertree arrays must be contiguous [S, depths, w]")
+    dev = sel_parent.device
+    n = int(budget) + 1
+    if out is None:
+        out = (torch.empty((S, n), dtype=torch.int32, device=dev), torch.empty((S, n), dtype=torch.int32, device=dev),
+               torch.empty((S, n), dtype=torch.int32, device=dev), torch.empty((S, n), dtype=torch.float32, device=dev),
+               torch.empty(S, dtype=torch.int32, device=dev))
+    st = _lib.load().dt_prune_topb(S, depths, w, int(budget), sel_parent.data_ptr(), sel_token.data_ptr(),
+                                   sel_score.data_ptr(), root_token.data_ptr(), *[t.data_ptr() for t in out],
+                                   _stream(stream))
+    _check(st, "dt_prune_topb")
+    return out

@@ -84,6 +84,11 @@ SIGNATURES = {
                                       c_p, c_size, c_p]),
     "dt_accept_path": (ctypes.c_int, [c_i32, P_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "dt_commit_kv": (ctypes.c_int, [ctypes.POINTER(dt_commit_desc), P_vp, P_vp, P_vp, P_vp, c_p, c_p, c_p]),
+    "dt_topk_rows_workspace_size": (ctypes.c_int, [c_i64, c_i64, c_i32, ctypes.POINTER(c_size)]),
+    "dt_topk_rows": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, c_i32, c_p, c_p, c_p, c_size, c_p]),
+    "dt_expand_depth": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, ctypes.c_float, c_p, c_i64, c_p, c_i64, c_p, c_i64,
+                                       c_p, c_p, c_p, c_p, c_i64, c_p]),
+    "dt_prune_topb": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
 }
 
 _lib = None

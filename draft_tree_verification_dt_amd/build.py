@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdtree.so")
 
-SOURCES = ["host.cpp", "attention.hip", "argmax.hip", "accept.hip", "commit.hip"]
+SOURCES = ["host.cpp", "attention.hip", "argmax.hip", "accept.hip", "commit.hip", "dartree.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated.

@@ -1,0 +1,643 @@
+// DARTree tree construction on the GPU: per-depth top-K candidates, depth-wise
+// fixed-width expansion and deferred top-B pruning (DARTree paper, Methodology:
+// Depth-Wise Parallel Supertree Construction, Algorithm 1, and Deferred
+// Best-First Pruning, eq. 5-6 with Lemma 1).
+//
+// All three are selections "the best m of M candidates" under a total order
+// (value descending, then a candidate index ascending). One block-wide routine
+// does them all: a most-significant-digit radix select (four 8-bit passes with
+// an LDS histogram) finds the m-th best value, a second radix select over the
+// candidate indices of the elements equal to it resolves ties by lowest index,
+// and the selected elements are gathered and, where the caller needs them in
+// order, sorted with a bitonic network in LDS. No pass depends on the data's
+// distribution, and exact ties are handled, so the result is the definition's.
+//
+//   topk_chunks + topk_merge   C_d = TopK(L_d, K) over the vocabulary, with the
+//                              log-softmax value of every kept token (the row's
+//                              log-sum-exp is merged from per-chunk (max, sum))
+//   expand_kernel              one depth: scores (s_parent + log q~) + beta of all
+//                              W_prev x K children, the best W kept in order
+//   prune_kernel               the best B supertree nodes by (score, depth,
+//                              slot), flattened into a verification tree
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace dt {
+namespace {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelMaxCand = 16384;  // candidates one block selects from (64 per thread)
+constexpr int kSelPerThread = kSelMaxCand / kSelThreads;
+constexpr int kTopkChunk = 4096;    // vocabulary entries per chunk workgroup (16 per thread)
+constexpr int kMaxSortedK = 1024;   // largest selection that is returned in order
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key); -0 is first made +0 so that the two compare equal, as floats do.
+__device__ inline uint32_t float_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+struct SelShared {
+  uint32_t hist[256];
+  uint32_t red[kSelThreads / 64];
+  uint32_t bin;
+  uint32_t remaining;
+  uint32_t count;
+};
+
+__device__ inline uint32_t block_sum_u32(uint32_t v, SelShared& sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) t += sh.red[w];
+  return t;
+}
+
+// The m-th largest key (1 <= m <= number of valid elements) among this block's
+// valid elements, and how many elements equal to it belong to the best m.
+template <int E>
+__device__ void radix_select(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t m, SelShared& sh,
+                             uint32_t& thr, uint32_t& need_eq) {
+  uint32_t prefix = 0, mask = 0, remaining = m;
+  const int lane = threadIdx.x & 63;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[threadIdx.x] = 0;  // 256 threads, 256 bins
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (valid[e] && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds bins 4l .. 4l+3; find the bin where the count from the top reaches `remaining`
+      const uint32_t c0 = sh.hist[4 * lane], c1 = sh.hist[4 * lane + 1], c2 = sh.hist[4 * lane + 2],
+                     c3 = sh.hist[4 * lane + 3];
+      const uint32_t s = c0 + c1 + c2 + c3;
+      uint32_t incl = s;  // sum over lanes >= this one
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(incl, off);
+        if (lane + off < 64) incl += o;
+      }
+      uint32_t cum = incl - s;  // elements in higher bins
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (cum < remaining && cum + cs[j] >= remaining) {
+          sh.bin = 4 * lane + j;
+          sh.remaining = remaining - cum;
+        }
+        cum += cs[j];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.bin << shift;
+    mask |= 0xFFu << shift;
+    remaining = sh.remaining;
+    __syncthreads();
+  }
+  thr = prefix;
+  need_eq = remaining;
+}
+
+// Select the best m valid elements by (key desc, idx asc) and append them,
+// unordered, to out_key/out_idx (LDS or global) through sh.count. Returns the
+// number selected: min(m, valid count). Indices of valid elements are unique.
+template <int E>
+__device__ uint32_t block_select(const uint32_t (&key)[E], const int32_t (&idx)[E], const bool (&valid)[E],
+                                 uint32_t m, SelShared& sh, uint32_t* out_key, int32_t* out_idx) {
+  uint32_t nv = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) nv += valid[e] ? 1u : 0u;
+  const uint32_t total = block_sum_u32(nv, sh);
+  const uint32_t take = std::min(m, total);
+  bool sel[E];
+  if (take == total || take == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = take != 0 && valid[e];
+  } else {
+    uint32_t thr, need_eq;
+    radix_select<E>(key, valid, take, sh, thr, need_eq);
+    uint32_t neq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == thr) ? 1u : 0u;
+    const uint32_t eq_total = block_sum_u32(neq, sh);
+    uint32_t idx_thr = 0xFFFFFFFFu;  // equal elements with idx <= idx_thr are taken
+    if (eq_total > need_eq) {
+      uint32_t ikey[E];
+      bool iv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ikey[e] = ~(uint32_t)idx[e];  // the largest ~idx are the smallest idx
+        iv[e] = valid[e] && key[e] == thr;
+      }
+      uint32_t t2, unused;
+      radix_select<E>(ikey, iv, need_eq, sh, t2, unused);
+      idx_thr = ~t2;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      sel[e] = valid[e] && (key[e] > thr || (key[e] == thr && (uint32_t)idx[e] <= idx_thr));
+  }
+  if (threadIdx.x == 0) sh.count = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (sel[e]) {
+      const uint32_t pos = atomicAdd(&sh.count, 1u);
+      out_key[pos] = key[e];
+      out_idx[pos] = idx[e];
+    }
+  __syncthreads();
+  return take;
+}
+
+// Is (ka, ia) ahead of (kb, ib)? Larger key, then smaller index.
+__device__ inline bool ahead(uint32_t ka, int32_t ia, uint32_t kb, int32_t ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Sort n (a power of two, <= kMaxSortedK) LDS entries best first.
+__device__ void bitonic_sort(uint32_t* k, int32_t* ix, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n / 2; i += kSelThreads) {
+        const int a = 2 * i - (i & (stride - 1));
+        const int b = a + stride;
+        const bool best_first = (a & size) == 0;
+        const bool b_ahead = ahead(k[b], ix[b], k[a], ix[a]);
+        if (b_ahead == best_first) {
+          const uint32_t tk = k[a];
+          k[a] = k[b];
+          k[b] = tk;
+          const int32_t ti = ix[a];
+          ix[a] = ix[b];
+          ix[b] = ti;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ inline int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------- top-K of rows
+
+struct TopkParams {
+  const float* x;
+  int64_t vocab, stride;
+  int32_t k, chunks;
+  uint32_t* part_key;   // [rows][chunks][k]
+  int32_t* part_idx;    // [rows][chunks][k]
+  float2* part_stat;    // [rows][chunks]: (chunk max, sum of exp(x - max))
+  int32_t* out_token;   // [rows][k]
+  float* out_logprob;   // [rows][k]
+};
+
+// grid (chunks, rows): the chunk's best k entries and its (max, sum exp) pair.
+template <bool VEC>
+__global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
+  __shared__ SelShared sh;
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const float* xr = p.x + row * p.stride;
+  const int64_t beg = (int64_t)c * kTopkChunk;
+  constexpr int E = kTopkChunk / kSelThreads;  // 16
+  float v[E];
+  uint32_t key[E];
+  int32_t idx[E];
+  bool valid[E];
+  // entry e of thread t: 4 * (t + 256 * (e / 4)) + e % 4 within the chunk (16-byte loads, coalesced)
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    const int64_t i0 = beg + 4 * ((int64_t)threadIdx.x + kSelThreads * q);
+    if (VEC && i0 + 3 < p.vocab) {
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
+      v[4 * q] = t.x;
+      v[4 * q + 1] = t.y;
+      v[4 * q + 2] = t.z;
+      v[4 * q + 3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = i0 + j < p.vocab ? xr[i0 + j] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      idx[4 * q + j] = (int32_t)(i0 + j);
+      valid[4 * q + j] = i0 + j < p.vocab;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (valid[e]) m = fmaxf(m, v[e]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wm[kSelThreads / 64], ws[kSelThreads / 64];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (valid[e]) s += __expf(v[e] - m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = float_key(v[e]);
+  __syncthreads();
+  const size_t base = ((size_t)row * p.chunks + c) * p.k;
+  if (threadIdx.x == 0) p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, (ws[0] + ws[1]) + (ws[2] + ws[3]));
+  const uint32_t got = block_select<E>(key, idx, valid, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base);
+  for (int j = (int)got + threadIdx.x; j < p.k; j += kSelThreads) {  // a short last chunk: pad
+    p.part_key[base + j] = 0u;
+    p.part_idx[base + j] = -1;
+  }
+}
+
+// grid (rows): merge the chunks' candidates and statistics; k best in order.
+__global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t sk[kMaxSortedK];
+  __shared__ int32_t si[kMaxSortedK];
+  __shared__ float red[kSelThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int M = p.chunks * p.k;
+  const size_t base = (size_t)row * M;
+  // log-sum-exp of the row from the chunk pairs
+  float m = -INFINITY;
+  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) m = fmaxf(m, p.part_stat[(size_t)row * p.chunks + c].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float s = 0.f;
+  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) {
+    const float2 st = p.part_stat[(size_t)row * p.chunks + c];
+    s += st.y * __expf(st.x - m);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
+  constexpr int E = kSelPerThread;
+  uint32_t key[E];
+  int32_t idx[E];
+  bool valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = threadIdx.x + kSelThreads * e;
+    const bool in = j < M;
+    key[e] = in ? p.part_key[base + j] : 0u;
+    idx[e] = in ? p.part_idx[base + j] : -1;
+    valid[e] = in && idx[e] >= 0;
+  }
+  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.k, sh, sk, si);
+  const int n = pow2_at_least(got);
+  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
+    sk[j] = 0u;
+    si[j] = INT_MAX;
+  }
+  __syncthreads();
+  bitonic_sort(sk, si, n);
+  for (int j = threadIdx.x; j < p.k; j += kSelThreads) {
+    const bool ok = j < got;
+    p.out_token[row * p.k + j] = ok ? si[j] : -1;
+    p.out_logprob[row * p.k + j] = ok ? key_float(sk[j]) - lse : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- one depth of expansion
+
+struct ExpandParams {
+  const float* parent_score;  // [S] rows of w_prev, stride ps_stride
+  const float* child_logq;    // [S][w_prev][k] rows, stride lq_stride
+  const int32_t* cand_token;  // [S] rows of k, stride ct_stride
+  int32_t* sel_parent;        // [S] rows of w, stride out_stride (same for the four outputs)
+  int32_t* sel_cand;
+  int32_t* sel_token;
+  float* sel_score;
+  int64_t ps_stride, lq_stride, ct_stride, out_stride;
+  int32_t w_prev, k, w;
+  float beta;
+};
+
+// grid (S): scores of every (parent slot p, candidate c) child, index p * k + c,
+// and the w best by (score desc, index asc), written in that order.
+__global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams p) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t sk[kMaxSortedK];
+  __shared__ int32_t si[kMaxSortedK];
+  const int64_t s = blockIdx.x;
+  const float* ps = p.parent_score + s * p.ps_stride;
+  const float* lq = p.child_logq + s * p.lq_stride;
+  const int M = p.w_prev * p.k;
+  constexpr int E = kSelPerThread;
+  uint32_t key[E];
+  int32_t idx[E];
+  bool valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = threadIdx.x + kSelThreads * e;
+    float sc = -INFINITY;
+    if (j < M) {
+      const int par = j / p.k;
+      const float a = ps[par] + lq[j];  // Algorithm 1, line 8, in this order
+      sc = a + p.beta;
+    }
+    key[e] = float_key(sc);
+    idx[e] = j;
+    valid[e] = j < M && isfinite(sc);
+  }
+  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.w, sh, sk, si);
+  const int n = pow2_at_least(got);
+  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
+    sk[j] = 0u;
+    si[j] = INT_MAX;
+  }
+  __syncthreads();
+  bitonic_sort(sk, si, n);
+  const int64_t o = s * p.out_stride;
+  for (int j = threadIdx.x; j < p.w; j += kSelThreads) {
+    const bool ok = j < got;
+    const int child = ok ? si[j] : 0;
+    const int c = child % p.k;
+    p.sel_parent[o + j] = ok ? child / p.k : -1;
+    p.sel_cand[o + j] = ok ? c : -1;
+    p.sel_token[o + j] = ok ? p.cand_token[s * p.ct_stride + c] : -1;
+    p.sel_score[o + j] = ok ? key_float(sk[j]) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- deferred top-B
+
+struct PruneParams {
+  const int32_t* sel_parent;  // [S][depths][w]
+  const int32_t* sel_token;
+  const float* sel_score;
+  const int32_t* root_token;  // [S]
+  int32_t* parent;            // [S][budget + 1]
+  int32_t* token;
+  int32_t* depth;
+  float* score;
+  int32_t* n_out;             // [S]
+  int32_t depths, w, budget;
+};
+
+// grid (S): the best `budget` supertree nodes by (score desc, depth asc, slot
+// asc) -- node index (d - 1) * w + slot orders depth, then slot -- flattened
+// after the root in that order.
+__global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t sk[kMaxSortedK];
+  __shared__ int32_t si[kMaxSortedK];
+  __shared__ int16_t newpos[kSelMaxCand];  // supertree node -> row in the output (-1: not kept)
+  __shared__ int bad;
+  const int64_t s = blockIdx.x;
+  const int M = p.depths * p.w;
+  const int32_t* spar = p.sel_parent + s * M;
+  const int32_t* stok = p.sel_token + s * M;
+  const float* ssc = p.sel_score + s * M;
+  constexpr int E = kSelPerThread;
+  uint32_t key[E];
+  int32_t idx[E];
+  bool valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = threadIdx.x + kSelThreads * e;
+    const bool in = j < M;
+    const float sc = in ? ssc[j] : -INFINITY;
+    const int32_t pr = in ? spar[j] : -1;
+    key[e] = float_key(sc);
+    idx[e] = j;
+    valid[e] = in && pr >= 0 && pr < p.w && isfinite(sc);
+  }
+  for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
+  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.budget, sh, sk, si);
+  const int n = pow2_at_least(got);
+  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
+    sk[j] = 0u;
+    si[j] = INT_MAX;
+  }
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  bitonic_sort(sk, si, n);
+  for (int j = threadIdx.x; j < got; j += kSelThreads) newpos[si[j]] = (int16_t)(j + 1);
+  __syncthreads();
+  // With beta <= 0 and log-probabilities <= 0 a child never precedes its parent
+  // (Lemma 1); check it, and keep only nodes whose parent is kept before them if not.
+  for (int j = threadIdx.x; j < got; j += kSelThreads) {
+    const int node = si[j];
+    const int d = node / p.w + 1;
+    if (d > 1) {
+      const int pp = newpos[(d - 2) * p.w + spar[node]];
+      if (pp < 0 || pp > j) bad = 1;
+    }
+  }
+  __syncthreads();
+  int kept = got;
+  if (bad) {  // violated device contract: a sequential, prefix-closed subset
+    if (threadIdx.x == 0) {
+      for (int j = 0; j < M; ++j) newpos[j] = -1;
+      int cnt = 0;
+      for (int j = 0; j < got; ++j) {
+        const int node = si[j];
+        const int d = node / p.w + 1;
+        const int pp = d > 1 ? newpos[(d - 2) * p.w + spar[node]] : 0;
+        if (pp >= 0) {
+          si[cnt] = node;
+          newpos[node] = (int16_t)(cnt + 1);
+          ++cnt;
+        }
+      }
+      sh.count = (uint32_t)cnt;
+    }
+    __syncthreads();
+    kept = (int)sh.count;
+  }
+  const int64_t o = s * (int64_t)(p.budget + 1);
+  if (threadIdx.x == 0) {
+    p.parent[o] = -1;
+    p.token[o] = p.root_token[s];
+    p.depth[o] = 0;
+    p.score[o] = 0.f;
+    p.n_out[s] = kept + 1;
+  }
+  for (int j = threadIdx.x; j < p.budget; j += kSelThreads) {
+    const int64_t r = o + 1 + j;
+    if (j < kept) {
+      const int node = si[j];
+      const int d = node / p.w + 1;
+      p.parent[r] = d > 1 ? newpos[(d - 2) * p.w + spar[node]] : 0;
+      p.token[r] = stok[node];
+      p.depth[r] = d;
+      p.score[r] = ssc[node];
+    } else {
+      p.parent[r] = -1;
+      p.token[r] = -1;
+      p.depth[r] = -1;
+      p.score[r] = -INFINITY;
+    }
+  }
+}
+
+int topk_plan(int64_t rows, int64_t vocab, int32_t k, int* chunks) {
+  if (rows < 0 || vocab < 1 || vocab > INT_MAX) return DT_ERR_SHAPE;
+  if (k < 1 || k > vocab) return DT_ERR_SHAPE;
+  if (k > kMaxSortedK || rows > 65535) return DT_ERR_UNSUPPORTED;
+  const int64_t c = ceil_div(vocab, kTopkChunk);
+  if (c * k > kSelMaxCand || c > 65535) return DT_ERR_UNSUPPORTED;
+  *chunks = (int)c;
+  return DT_OK;
+}
+
+size_t topk_ws_bytes(int64_t rows, int chunks, int32_t k) {
+  const size_t cand = (size_t)rows * chunks * k;
+  return round_up(cand * 4, 256) + round_up(cand * 4, 256) + round_up((size_t)rows * chunks * sizeof(float2), 256);
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_topk_rows_workspace_size(int64_t rows, int64_t vocab, int32_t k, size_t* bytes) {
+  if (!bytes) return DT_ERR_NULL;
+  int chunks = 0;
+  const int st = dt::topk_plan(rows, vocab, k, &chunks);
+  if (st != DT_OK) return st;
+  *bytes = dt::topk_ws_bytes(rows, chunks, k);
+  return DT_OK;
+}
+
+extern "C" int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t k,
+                            int32_t* out_token, float* out_logprob, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  using namespace dt;
+  int chunks = 0;
+  int st = topk_plan(rows, vocab, k, &chunks);
+  if (st != DT_OK) return st;
+  if (row_stride < vocab) return DT_ERR_SHAPE;
+  if (rows == 0) return DT_OK;
+  if (!logits || !out_token || !out_logprob) return DT_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(out_token, 4) || !aligned(out_logprob, 4)) return DT_ERR_SHAPE;
+  const size_t need = topk_ws_bytes(rows, chunks, k);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return DT_ERR_WORKSPACE;
+  const size_t cand = (size_t)rows * chunks * k;
+  char* ws = static_cast<char*>(workspace);
+  TopkParams p;
+  p.x = logits;
+  p.vocab = vocab;
+  p.stride = row_stride;
+  p.k = k;
+  p.chunks = chunks;
+  p.part_key = reinterpret_cast<uint32_t*>(ws);
+  p.part_idx = reinterpret_cast<int32_t*>(ws + round_up(cand * 4, 256));
+  p.part_stat = reinterpret_cast<float2*>(ws + 2 * round_up(cand * 4, 256));
+  p.out_token = out_token;
+  p.out_logprob = out_logprob;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vec = aligned(logits, 16) && row_stride % 4 == 0;
+  if (vec)
+    hipLaunchKernelGGL(topk_chunks<true>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_chunks<false>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
+  hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+  return launch_status();
+}
+
+extern "C" int dt_expand_depth(int32_t num_seqs, int32_t w_prev, int32_t k, int32_t w, float beta,
+                               const float* parent_score, int64_t parent_score_stride, const float* child_logq,
+                               int64_t child_logq_stride, const int32_t* cand_token, int64_t cand_token_stride,
+                               int32_t* sel_parent, int32_t* sel_cand, int32_t* sel_token, float* sel_score,
+                               int64_t out_stride, void* stream) {
+  using namespace dt;
+  if (num_seqs < 0 || w_prev < 1 || k < 1 || w < 1) return DT_ERR_SHAPE;
+  if ((int64_t)w_prev * k > kSelMaxCand || w > kMaxSortedK || num_seqs > 65535) return DT_ERR_UNSUPPORTED;
+  if (!(beta <= 0.f) || !std::isfinite(beta)) return DT_ERR_VALUE;
+  if (parent_score_stride < w_prev || child_logq_stride < (int64_t)w_prev * k || cand_token_stride < k ||
+      out_stride < w)
+    return DT_ERR_SHAPE;
+  if (num_seqs == 0) return DT_OK;
+  if (!parent_score || !child_logq || !cand_token || !sel_parent || !sel_cand || !sel_token || !sel_score)
+    return DT_ERR_NULL;
+  if (!aligned(parent_score, 4) || !aligned(child_logq, 4) || !aligned(cand_token, 4) || !aligned(sel_parent, 4) ||
+      !aligned(sel_cand, 4) || !aligned(sel_token, 4) || !aligned(sel_score, 4))
+    return DT_ERR_SHAPE;
+  ExpandParams p;
+  p.parent_score = parent_score;
+  p.child_logq = child_logq;
+  p.cand_token = cand_token;
+  p.sel_parent = sel_parent;
+  p.sel_cand = sel_cand;
+  p.sel_token = sel_token;
+  p.sel_score = sel_score;
+  p.ps_stride = parent_score_stride;
+  p.lq_stride = child_logq_stride;
+  p.ct_stride = cand_token_stride;
+  p.out_stride = out_stride;
+  p.w_prev = w_prev;
+  p.k = k;
+  p.w = w;
+  p.beta = beta;
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, static_cast<hipStream_t>(stream),
+                     p);
+  return launch_status();
+}
+
+extern "C" int dt_prune_topb(int32_t num_seqs, int32_t depths, int32_t w, int32_t budget, const int32_t* sel_parent,
+                             const int32_t* sel_token, const float* sel_score, const int32_t* root_token,
+                             int32_t* parent, int32_t* token, int32_t* depth, float* score, int32_t* n_out,
+                             void* stream) {
+  using namespace dt;
+  if (num_seqs < 0 || depths < 1 || w < 1 || budget < 0) return DT_ERR_SHAPE;
+  if ((int64_t)depths * w > kSelMaxCand || budget + 1 > DT_MAX_TREE_NODES || num_seqs > 65535)
+    return DT_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return DT_OK;
+  if (!sel_parent || !sel_token || !sel_score || !root_token || !parent || !token || !depth || !score || !n_out)
+    return DT_ERR_NULL;
+  if (!aligned(sel_parent, 4) || !aligned(sel_token, 4) || !aligned(sel_score, 4) || !aligned(root_token, 4) ||
+      !aligned(parent, 4) || !aligned(token, 4) || !aligned(depth, 4) || !aligned(score, 4) || !aligned(n_out, 4))
+    return DT_ERR_SHAPE;
+  PruneParams p;
+  p.sel_parent = sel_parent;
+  p.sel_token = sel_token;
+  p.sel_score = sel_score;
+  p.root_token = root_token;
+  p.parent = parent;
+  p.token = token;
+  p.depth = depth;
+  p.score = score;
+  p.n_out = n_out;
+  p.depths = depths;
+  p.w = w;
+  p.budget = budget;
+  hipLaunchKernelGGL(prune_kernel, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, static_cast<hipStream_t>(stream),
+                     p);
+  return launch_status();
+}

@@ -19,6 +19,9 @@
  *   dt_sample_rows      GPU:  per-node target sample at temperature T > 0 (Gumbel-max)
  *   dt_accept_path      GPU:  longest accepted path and bonus token
  *   dt_commit_kv        GPU:  accepted path's K/V into the KV cache, all layers
+ *   dt_topk_rows        GPU:  per-depth top-K draft candidates with log-softmax values
+ *   dt_expand_depth     GPU:  one depth of DARTree's fixed-width supertree
+ *   dt_prune_topb       GPU:  deferred top-B pruning into the verification tree
  *
  * Conventions shared by every entry point
  *  - Every function returns an int status: DT_OK (0) or a negative DT_ERR_*.
@@ -339,6 +342,105 @@ typedef struct dt_commit_desc {
 int dt_commit_kv(const dt_commit_desc* desc, const void* const* k_tree, const void* const* v_tree,
                  void* const* k_cache, void* const* v_cache, const int32_t* path, const int32_t* accept_len,
                  void* stream);
+
+/*
+ * DARTree tree construction (GPU): the drafter's per-depth candidates, the
+ * depth-wise fixed-width expansion and the deferred top-B pruning of DARTree
+ * paper, Methodology (Depth-Wise Parallel Supertree Construction, Algorithm 1;
+ * Deferred Best-First Pruning, eq. 5-6 and Lemma 1). The correction head that
+ * scores candidates under each prefix (Algorithm 1, lines 5-6) is a trained
+ * network and stays with the caller: it turns the retained prefixes of depth
+ * d-1 into log q~ values for every (prefix, candidate) pair, which
+ * dt_expand_depth consumes.
+ */
+
+/*
+ * dt_topk_rows_workspace_size -- device workspace of dt_topk_rows.
+ */
+int dt_topk_rows_workspace_size(int64_t rows, int64_t vocab, int32_t k, size_t* bytes);
+
+/*
+ * dt_topk_rows -- C_d = TopK(L_d, K): the k best entries of every row, in
+ * order, with their log-softmax values (GPU).
+ *
+ * Defined by: DARTree paper, Depth-Wise Parallel Supertree Construction (only
+ * the drafter's top-K token predictions at each position are candidate
+ * extensions) and Algorithm 1, line 4. Per row r: out_token[r][0..k-1] are the
+ * indices of the k largest logits ordered by (logit descending, index
+ * ascending; -0 == +0), and out_logprob[r][j] = logits[r][out_token[r][j]] -
+ * log(sum_v exp(logits[r][v])) in fp32. The same table, one row per draft
+ * position, is the candidate input of dt_build_tree.
+ *   logits     device float32, rows x vocab, row stride >= vocab (4-byte
+ *              aligned; 16-byte rows read faster). Contract: finite values.
+ *   rows       0 .. 65535 (0 is a no-op); 1 <= k <= min(vocab, 1024), and
+ *              ceil(vocab / 4096) * k <= 16384 (DT_ERR_UNSUPPORTED otherwise)
+ *   out_token  device int32 [rows][k]; out_logprob device float32 [rows][k]
+ *   workspace  >= dt_topk_rows_workspace_size bytes, 256-byte aligned.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_UNSUPPORTED, DT_ERR_WORKSPACE, DT_ERR_HIP.
+ */
+int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, int32_t k,
+                 int32_t* out_token, float* out_logprob, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dt_expand_depth -- one depth of DARTree's fixed-width supertree (GPU).
+ *
+ * Defined by: DARTree paper, Algorithm 1, lines 7-9, with eq. 5's score. For
+ * every sequence s, every retained prefix (slot p < w_prev of depth d-1, score
+ * parent_score[p]) and every candidate c < k of depth d, the child scores
+ *   score(p, c) = (parent_score[p] + child_logq[p][c]) + beta      (fp32, in this order)
+ * and the w children with the highest scores are kept, ordered by (score
+ * descending, p ascending, c ascending). Children whose score is not finite
+ * (e.g. an absent parent slot with score -inf) are never kept; when fewer than
+ * w remain, the extra output slots get parent = cand = token = -1 and score -inf.
+ *   parent_score  device float [S] rows of w_prev, row stride parent_score_stride
+ *                 (depth 1: the root alone, w_prev = 1, score 0)
+ *   child_logq    device float [S] rows of w_prev * k (row-major [p][c]), row
+ *                 stride child_logq_stride: the correction head's log q~
+ *   cand_token    device int32 [S] rows of k (stride cand_token_stride): the
+ *                 candidates' tokens, e.g. dt_topk_rows' output for this depth
+ *   sel_parent, sel_cand, sel_token, sel_score  device [S] rows of w, row
+ *                 stride out_stride: the kept children (their scores are the
+ *                 next depth's parent_score)
+ *   beta          depth bonus, <= 0 and finite (Algorithm 1 requires beta <= 0)
+ * Limits: w_prev * k <= 16384, w <= 1024, S <= 65535 (DT_ERR_UNSUPPORTED).
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_VALUE (beta), DT_ERR_UNSUPPORTED, DT_ERR_HIP.
+ */
+int dt_expand_depth(int32_t num_seqs, int32_t w_prev, int32_t k, int32_t w, float beta, const float* parent_score,
+                    int64_t parent_score_stride, const float* child_logq, int64_t child_logq_stride,
+                    const int32_t* cand_token, int64_t cand_token_stride, int32_t* sel_parent, int32_t* sel_cand,
+                    int32_t* sel_token, float* sel_score, int64_t out_stride, void* stream);
+
+/*
+ * dt_prune_topb -- deferred top-B pruning of the supertree into the
+ * verification tree (GPU).
+ *
+ * Defined by: DARTree paper, Deferred Best-First Pruning, eq. 6 and Lemma 1
+ * (with beta <= 0 and ancestors preferred on ties, the best-first heap over the
+ * supertree equals its global top-B by s_beta), and Algorithm 1, line 12.
+ * The supertree of sequence s is depths layers of w slots (dt_expand_depth's
+ * outputs, layer d-1 at offset (d-1)*w): slot j of depth d is the child of slot
+ * sel_parent of depth d-1 (depth 1: of the root), carries sel_token and
+ * sel_score; slots with sel_parent < 0 or a non-finite score are empty. The
+ * call keeps the budget best nodes by (score descending, depth ascending, slot
+ * ascending) and writes the tree root first, then those nodes in that order,
+ * which lists every parent before its children:
+ *   parent[s][i] (tree-local, parent[s][0] = -1), token[s][i] (token[s][0] =
+ *   root_token[s]), depth[s][i], score[s][i] (score[s][0] = 0) for
+ *   i < n_out[s] = 1 + min(budget, non-empty slots); rows past n_out[s] get
+ *   parent = token = depth = -1, score -inf.
+ *   sel_parent, sel_token, sel_score  device [S][depths][w]
+ *   root_token  device int32 [S]
+ *   parent, token, depth, score  device [S][budget + 1]; n_out device int32 [S]
+ * Contract: the log q~ behind the scores are <= 0 and beta <= 0 (then every
+ * child scores at most its parent, Lemma 1). If the device data break it, the
+ * output is still a tree: a kept node whose parent is not kept before it is
+ * dropped.
+ * Limits: depths * w <= 16384, budget + 1 <= DT_MAX_TREE_NODES, S <= 65535.
+ * Errors: DT_ERR_NULL, DT_ERR_SHAPE, DT_ERR_UNSUPPORTED, DT_ERR_HIP.
+ */
+int dt_prune_topb(int32_t num_seqs, int32_t depths, int32_t w, int32_t budget, const int32_t* sel_parent,
+                  const int32_t* sel_token, const float* sel_score, const int32_t* root_token, int32_t* parent,
+                  int32_t* token, int32_t* depth, float* score, int32_t* n_out, void* stream);
 
 #ifdef __cplusplus
 }

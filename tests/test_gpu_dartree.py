@@ -1,0 +1,280 @@
+"""GPU parity of DARTree's construction kernels against the oracle:
+dt_topk_rows (tokens bit-exact, log-softmax values within fp32 rounding),
+dt_expand_depth and dt_prune_topb (bit-exact: both sides take every decision
+on the same fp32 scores), a whole depth-wise construction with a synthetic
+path-dependent correction head, and the DDTree special case against the host
+best-first builder (Lemma 1)."""
+
+import numpy as np
+import pytest
+
+import draft_tree_verification_dt_amd as dt
+from _helpers import dev_i32, require_gpu
+from gen import rng as grng
+from oracle import dartree as odt, tree as otree
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _t(a, dtype=None):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a if dtype is None else a.astype(dtype))).cuda()
+
+
+def _check_topk(x, k, pad=0):
+    import torch
+
+    rows, vocab = x.shape
+    buf = torch.full((rows, vocab + pad), float("inf"), dtype=torch.float32, device="cuda")
+    buf[:, :vocab] = _t(x)
+    tok, lp = dt.dt_topk_rows(buf[:, :vocab], k)
+    torch.cuda.synchronize()
+    want_t, want_lp = odt.topk_logprobs(x, k)
+    np.testing.assert_array_equal(tok.cpu().numpy(), want_t)
+    got = lp.cpu().numpy().astype(np.float64)
+    tol = 2e-5 + 2e-6 * np.abs(want_lp)
+    assert (np.abs(got - want_lp) <= tol).all(), float(np.abs(got - want_lp).max())
+
+
+@pytest.mark.parametrize("rows,vocab,k", [(1, 1, 1), (3, 7, 7), (5, 4097, 64), (16, 151936, 64), (16, 151936, 256),
+                                          (2, 262144, 256), (7, 1000, 1), (4, 8192, 1024), (33, 5000, 17)])
+def test_topk_matches_oracle(rows, vocab, k):
+    require_gpu()
+    x = (grng.stream(rows, vocab, k, "topk").standard_normal((rows, vocab)) * 3).astype(np.float32)
+    print(f"topk rows={rows} vocab={vocab} k={k}", flush=True)
+    _check_topk(x, k)
+
+
+@pytest.mark.parametrize("pad", [1, 3])
+def test_topk_strided_rows(pad):
+    require_gpu()
+    x = grng.stream(pad, "topk-stride").standard_normal((9, 10001)).astype(np.float32)
+    print(f"topk stride pad={pad}", flush=True)
+    _check_topk(x, 64, pad=pad)
+
+
+def test_topk_ties_and_special_values():
+    require_gpu()
+    r = grng.stream(5, "topk-ties")
+    x = r.standard_normal((6, 20000)).astype(np.float32)
+    x[0, :] = 1.0                                  # all equal: the k lowest indices
+    x[1, ::7] = 4.0                                # a large tie straddling the threshold and the chunks
+    x[2, :] = np.round(x[2] * 2) / 2               # few distinct levels
+    x[3, :100] = -0.0
+    x[3, 100:] = -5.0
+    x[3, 50] = 0.0                                 # signed zeros equal: index order
+    x[4, 19999] = 50.0                             # the last entry
+    x[5, 4095:4099] = 30.0                         # a tie across a chunk boundary
+    print("topk ties", flush=True)
+    _check_topk(x, 64)
+    _check_topk(x, 1000)
+
+
+def _random_expand_case(r, S, w_prev, k, ties):
+    ps = np.sort(-np.abs(r.standard_normal((S, w_prev))).astype(F32) * F32(3), axis=1)[:, ::-1].copy()
+    ps[:, 0] = F32(0.0) if w_prev == 1 else ps[:, 0]
+    if w_prev > 2:
+        ps[0, -2:] = -np.inf                       # absent parent slots
+    if ties:
+        lq = (-r.integers(0, 4, size=(S, w_prev, k)).astype(F32) * F32(0.5))
+    else:
+        lq = np.log(r.dirichlet(np.ones(k) * 0.5, size=(S, w_prev))).astype(F32)
+    ct = r.integers(0, 151936, size=(S, k)).astype(np.int32)
+    return ps, lq, ct
+
+
+@pytest.mark.parametrize("S,w_prev,k,w,beta,ties", [(1, 1, 64, 12, -0.2, False), (3, 12, 64, 12, -0.2, False),
+                                                     (2, 12, 64, 12, 0.0, True), (4, 5, 3, 40, -1.0, False),
+                                                     (2, 64, 256, 1024, -0.2, False), (2, 64, 256, 100, 0.0, True),
+                                                     (5, 7, 9, 1, -0.2, True)])
+def test_expand_matches_oracle(S, w_prev, k, w, beta, ties):
+    import torch
+
+    require_gpu()
+    r = grng.stream(S, w_prev, k, w, "expand-gpu")
+    ps, lq, ct = _random_expand_case(r, S, w_prev, k, ties)
+    print(f"expand S={S} w_prev={w_prev} k={k} w={w} beta={beta} ties={ties}", flush=True)
+    par, cand, tok, sc = dt.dt_expand_depth(_t(ps), _t(lq), _t(ct), w, beta)
+    torch.cuda.synchronize()
+    par, cand, tok, sc = (x.cpu().numpy() for x in (par, cand, tok, sc))
+    for s in range(S):
+        wp, wc, ws = odt.expand_depth(ps[s], lq[s], beta, w)
+        m = len(wp)
+        assert list(par[s, :m]) == wp and list(cand[s, :m]) == wc, s
+        np.testing.assert_array_equal(sc[s, :m].view(np.uint32), np.array(ws, F32).view(np.uint32))
+        assert list(tok[s, :m]) == [int(ct[s, c]) for c in wc]
+        assert (par[s, m:] == -1).all() and (cand[s, m:] == -1).all() and (tok[s, m:] == -1).all()
+        assert np.isneginf(sc[s, m:]).all()
+
+
+def _layers_to_arrays(layers_per_seq, depths, w, cand_tokens):
+    S = len(layers_per_seq)
+    par = np.full((S, depths, w), -1, np.int32)
+    tok = np.full((S, depths, w), -1, np.int32)
+    sc = np.full((S, depths, w), -np.inf, F32)
+    for s, layers in enumerate(layers_per_seq):
+        for d, layer in enumerate(layers):
+            for j, (p, c, v) in enumerate(layer):
+                par[s, d, j], tok[s, d, j], sc[s, d, j] = p, cand_tokens[s][d][c], v
+    return par, tok, sc
+
+
+def _random_layers(r, depths, w, k, beta, ties):
+    def head(paths):
+        if ties:
+            return -r.integers(0, 3, size=(len(paths), k)).astype(F32) * F32(0.5)
+        return np.log(r.dirichlet(np.ones(k) * 0.6, size=len(paths))).astype(F32)
+    return odt.build_supertree([head] * depths, beta, w)
+
+
+@pytest.mark.parametrize("S,depths,w,k,budget,beta,ties", [(1, 16, 12, 64, 64, -0.2, False), (3, 16, 12, 64, 64, 0.0, True),
+                                                           (2, 5, 8, 3, 1000, -0.2, False), (2, 16, 64, 64, 255, -0.2, False),
+                                                           (4, 3, 4, 2, 0, -0.2, False), (2, 16, 1024, 8, 1023, -0.1, False)])
+def test_prune_matches_oracle(S, depths, w, k, budget, beta, ties):
+    import torch
+
+    require_gpu()
+    r = grng.stream(S, depths, w, budget, "prune-gpu")
+    layers = [_random_layers(r, depths, w, k, beta, ties) for _ in range(S)]
+    ctok = [r.integers(0, 151936, size=(depths, k)) for _ in range(S)]
+    par, tok, sc = _layers_to_arrays(layers, depths, w, ctok)
+    roots = r.integers(0, 151936, size=S).astype(np.int32)
+    print(f"prune S={S} depths={depths} w={w} budget={budget} ties={ties}", flush=True)
+    gp, gt, gd, gs, gn = dt.dt_prune_topb(_t(par), _t(tok), _t(sc), _t(roots), budget)
+    torch.cuda.synchronize()
+    gp, gt, gd, gs, gn = (x.cpu().numpy() for x in (gp, gt, gd, gs, gn))
+    for s in range(S):
+        kept = odt.prune_topb(layers[s], budget)
+        assert kept == odt.best_first(layers[s], budget)  # Lemma 1 on this supertree
+        wp, wt, wd, ws = odt.tree_arrays(layers[s], kept, ctok[s])
+        n = len(kept)
+        assert gn[s] == n
+        wt[0] = roots[s]
+        assert list(gp[s, :n]) == list(wp) and list(gt[s, :n]) == list(wt) and list(gd[s, :n]) == list(wd)
+        np.testing.assert_array_equal(gs[s, :n].view(np.uint32), ws.view(np.uint32))
+        assert (gp[s, n:] == -1).all() and (gd[s, n:] == -1).all()
+        otree.check(gp[s, :n])
+
+
+def _synthetic_head(cand_logprob, paths, cands, strength=1.0):
+    """Stand-in for the correction head: the drafter's log-probabilities of the
+    candidates, shifted by a deterministic function of (the prefix, given as its
+    candidate ranks, and the candidate token) and renormalised over the
+    candidates (float32)."""
+    out = np.empty((len(paths), len(cands)), np.float64)
+    mask = (1 << 64) - 1
+    for i, path in enumerate(paths):
+        h = 1469598103934665603
+        for t in path:
+            h = ((h ^ (int(t) & 0xFFFFFFFF)) * 1099511628211) & mask
+        salt = ((np.asarray(cands, np.uint64) * np.uint64(2654435761) + np.uint64(h)) >> np.uint64(40))
+        salt = salt.astype(np.float64)
+        shift = strength * (salt / float(1 << 24) - 0.5)
+        z = cand_logprob.astype(np.float64) + shift
+        out[i] = z - (z.max() + np.log(np.exp(z - z.max()).sum()))
+    return out.astype(F32)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_dartree_construction_end_to_end(seed):
+    """gamma = 16 draft positions over a 151936-token vocabulary, K = 64, W = 12,
+    beta = -0.2, B = 64 (DARTree's pruned configuration): GPU top-K, sixteen GPU
+    expansions fed by a path-dependent synthetic head, GPU pruning; every step
+    equal to the oracle's, and the result a valid verification tree."""
+    import torch
+
+    require_gpu()
+    r = grng.stream(seed, "dartree-e2e")
+    S, gamma, V, K, W, B, beta = 2, 16, 151936, 64, 12, 64, -0.2
+    base = (r.standard_normal((S * gamma, V)) * 3).astype(np.float32)
+    print(f"dartree end-to-end seed={seed}", flush=True)
+    ctok_d, clp_d = dt.dt_topk_rows(_t(base), K)
+    torch.cuda.synchronize()
+    ctok = ctok_d.cpu().numpy().reshape(S, gamma, K)
+    clp = clp_d.cpu().numpy().reshape(S, gamma, K)
+    wt, wl = odt.topk_logprobs(base, K)
+    np.testing.assert_array_equal(ctok.reshape(-1, K), wt)
+    par_all = torch.full((S, gamma, W), -1, dtype=torch.int32, device="cuda")
+    cand_all = torch.full((S, gamma, W), -1, dtype=torch.int32, device="cuda")
+    tok_all = torch.full((S, gamma, W), -1, dtype=torch.int32, device="cuda")
+    sc_all = torch.full((S, gamma, W), float("-inf"), dtype=torch.float32, device="cuda")
+    prev_score = torch.zeros((S, 1), dtype=torch.float32, device="cuda")
+    paths = [[()] for _ in range(S)]
+    oracle_layers = []
+    for s in range(S):
+        heads = [(lambda d, s=s: (lambda ps: _synthetic_head(clp[s, d], ps, ctok[s, d])))(d) for d in range(gamma)]
+        oracle_layers.append(odt.build_supertree(heads, beta, W))
+    for d in range(gamma):
+        w_prev = len(paths[0])
+        lq = np.stack([_synthetic_head(clp[s, d], paths[s], ctok[s, d]) for s in range(S)])
+        out = (par_all[:, d], cand_all[:, d], tok_all[:, d], sc_all[:, d])
+        dt.dt_expand_depth(prev_score, _t(lq), ctok_d.view(S, gamma, K)[:, d], W, beta, out=out)
+        torch.cuda.synchronize()
+        par_h, cand_h = par_all[:, d].cpu().numpy(), cand_all[:, d].cpu().numpy()
+        for s in range(S):
+            want = oracle_layers[s][d]
+            assert list(zip(par_h[s][:len(want)], cand_h[s][:len(want)])) == [(p, c) for p, c, _ in want], (s, d)
+            paths[s] = [paths[s][p] + (int(c),) for p, c, _ in want]
+        prev_score = sc_all[:, d]
+        assert w_prev >= 1
+    roots = r.integers(0, V, size=S).astype(np.int32)
+    gp, gt, gd, gs, gn = dt.dt_prune_topb(par_all, tok_all, sc_all, _t(roots), B)
+    torch.cuda.synchronize()
+    gp, gt, gd, gn = gp.cpu().numpy(), gt.cpu().numpy(), gd.cpu().numpy(), gn.cpu().numpy()
+    for s in range(S):
+        kept = odt.prune_topb(oracle_layers[s], B)
+        wp, wtk, wd, _ = odt.tree_arrays(oracle_layers[s], kept, ctok[s])
+        wtk[0] = roots[s]
+        assert gn[s] == B + 1 and list(gp[s]) == list(wp) and list(gt[s]) == list(wtk) and list(gd[s]) == list(wd)
+        otree.check(gp[s])
+        assert gd[s].max() > 3  # the correction-driven supertree reaches real depth
+
+
+def test_factorised_head_equals_host_heap():
+    """DDTree as the special case: the same per-depth log-probabilities for every
+    parent, beta = 0 and a width that keeps every prefix; the GPU's deferred
+    top-B equals dt_build_tree's best-first heap node for node (Lemma 1)."""
+    import torch
+
+    require_gpu()
+    r = grng.stream(7, "factorised-gpu")
+    depths, k = 5, 3
+    ran = 0
+    for trial in range(6):
+        # multiples of 2^-18 below 4: sums over 5 depths stay exact in float32
+        lp = np.sort(-r.integers(1, 1 << 20, size=(depths, k)).astype(np.float64) / (1 << 18), axis=1)[:, ::-1]
+        lp = np.ascontiguousarray(lp.astype(np.float32))
+        tok = np.stack([r.choice(1000, size=k, replace=False) for _ in range(depths)]).astype(np.int32)
+        for d in range(depths):
+            order = np.lexsort((tok[d], -lp[d]))
+            lp[d], tok[d] = lp[d][order], tok[d][order]
+        W = k ** depths
+        par_all = torch.full((1, depths, W), -1, dtype=torch.int32, device="cuda")
+        cand_all = torch.full((1, depths, W), -1, dtype=torch.int32, device="cuda")
+        tok_all = torch.full((1, depths, W), -1, dtype=torch.int32, device="cuda")
+        sc_all = torch.full((1, depths, W), float("-inf"), dtype=torch.float32, device="cuda")
+        prev = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+        width = 1
+        for d in range(depths):
+            lq = np.tile(lp[d], (1, width, 1)).astype(F32)
+            dt.dt_expand_depth(prev, _t(lq), _t(tok[d:d + 1]), W, 0.0,
+                               out=(par_all[:, d], cand_all[:, d], tok_all[:, d], sc_all[:, d]))
+            width *= k
+            prev = sc_all[:, d, :width]
+        scores = sc_all.cpu().numpy()[np.isfinite(sc_all.cpu().numpy())]
+        if len(np.unique(scores)) < len(scores):
+            continue  # equal scores are ordered by slot here and by rank tuple in the heap
+        ran += 1
+        total = sum(k ** d for d in range(1, depths + 1))
+        for n in (1, 2, 17, 100, total + 1):
+            gp, gt, gd, gs, gn = dt.dt_prune_topb(par_all, tok_all, sc_all, dev_i32([77]), n - 1)
+            torch.cuda.synchronize()
+            hp, ht, hd, hs = dt.dt_build_tree(lp, tok, 77, n)
+            m = int(gn.cpu()[0])
+            assert m == len(hp)
+            assert list(gp.cpu().numpy()[0, :m]) == list(hp) and list(gt.cpu().numpy()[0, :m]) == list(ht)
+            assert list(gd.cpu().numpy()[0, :m]) == list(hd)
+            np.testing.assert_array_equal(gs.cpu().numpy()[0, :m].astype(np.float64), hs)
+    assert ran >= 3

@@ -233,3 +233,43 @@ def test_commit_validation_errors():
     assert lib.dt_commit_kv(ctypes.byref(d), ptrs(256, 0), good, good, good, 16, 16, None) == _lib.DT_ERR_NULL
     assert lib.dt_commit_kv(ctypes.byref(d), ptrs(256, 520), good, good, good, 16, 16, None) == _lib.DT_ERR_SHAPE
     assert lib.dt_commit_kv(ctypes.byref(d), good, good, good, good, 18, 16, None) == _lib.DT_ERR_SHAPE
+
+
+def test_dartree_validation_errors():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    ws = lib.dt_topk_rows_workspace_size
+    assert ws(16, 151936, 64, ctypes.byref(n)) == _lib.DT_OK and n.value > 0
+    assert ws(16, 151936, 0, ctypes.byref(n)) == _lib.DT_ERR_SHAPE
+    assert ws(16, 10, 11, ctypes.byref(n)) == _lib.DT_ERR_SHAPE                      # k > vocab
+    assert ws(16, 151936, 2000, ctypes.byref(n)) == _lib.DT_ERR_UNSUPPORTED
+    assert ws(16, 10 ** 6, 256, ctypes.byref(n)) == _lib.DT_ERR_UNSUPPORTED          # too many chunk candidates
+    assert ws(70000, 1000, 8, ctypes.byref(n)) == _lib.DT_ERR_UNSUPPORTED
+    tk = lib.dt_topk_rows
+    assert tk(16, 4, 100, 99, 8, 16, 16, 256, 1 << 20, None) == _lib.DT_ERR_SHAPE      # stride < vocab
+    assert tk(16, 0, 100, 100, 8, 16, 16, 256, 1 << 20, None) == _lib.DT_OK           # empty
+    assert tk(None, 4, 100, 100, 8, 16, 16, 256, 1 << 20, None) == _lib.DT_ERR_NULL
+    assert tk(16, 4, 100, 100, 8, 16, 16, None, 0, None) == _lib.DT_ERR_WORKSPACE
+    assert tk(16, 4, 100, 100, 8, 16, 16, 264, 1 << 20, None) == _lib.DT_ERR_WORKSPACE  # misaligned workspace
+    ex = lib.dt_expand_depth
+    good = (16, 12, 16, 768, 16, 64, 16, 16, 16, 16, 12)
+    for beta in (0.1, float("nan"), float("inf")):
+        assert ex(2, 12, 64, 12, beta, *good, None) == _lib.DT_ERR_VALUE, beta
+    assert ex(2, 12, 64, 0, -0.2, *good, None) == _lib.DT_ERR_SHAPE                 # w = 0
+    assert ex(2, 12, 64, 12, -0.2, 16, 11, 16, 768, 16, 64, 16, 16, 16, 16, 12, None) == _lib.DT_ERR_SHAPE
+    assert ex(2, 12, 64, 12, -0.2, 16, 12, 16, 700, 16, 64, 16, 16, 16, 16, 12, None) == _lib.DT_ERR_SHAPE
+    assert ex(2, 12, 64, 12, -0.2, 16, 12, 16, 768, 16, 64, 16, 16, 16, 16, 11, None) == _lib.DT_ERR_SHAPE
+    assert ex(2, 300, 64, 12, -0.2, 16, 300, 16, 19200, 16, 64, 16, 16, 16, 16, 12, None) == _lib.DT_ERR_UNSUPPORTED
+    assert ex(2, 12, 64, 2000, -0.2, 16, 12, 16, 768, 16, 64, 16, 16, 16, 16, 2000, None) == _lib.DT_ERR_UNSUPPORTED
+    assert ex(0, 12, 64, 12, -0.2, *good, None) == _lib.DT_OK
+    assert ex(2, 12, 64, 12, -0.2, None, *good[1:], None) == _lib.DT_ERR_NULL
+    assert ex(2, 12, 64, 12, -0.2, 18, *good[1:], None) == _lib.DT_ERR_SHAPE       # misaligned
+    pr = lib.dt_prune_topb
+    bufs = [16] * 9
+    assert pr(2, 0, 12, 64, *bufs, None) == _lib.DT_ERR_SHAPE
+    assert pr(2, 16, 12, -1, *bufs, None) == _lib.DT_ERR_SHAPE
+    assert pr(2, 16, 12, 1024, *bufs, None) == _lib.DT_ERR_UNSUPPORTED
+    assert pr(2, 200, 100, 64, *bufs, None) == _lib.DT_ERR_UNSUPPORTED
+    assert pr(0, 16, 12, 64, *bufs, None) == _lib.DT_OK
+    assert pr(2, 16, 12, 64, *([None] + bufs[1:]), None) == _lib.DT_ERR_NULL
+    assert pr(2, 16, 12, 64, *([18] + bufs[1:]), None) == _lib.DT_ERR_SHAPE
