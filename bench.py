@@ -296,6 +296,77 @@ def time_commit_calls(rnd, reps):
     return ms, moved, acc
 
 
+class DraftBuild:
+    """DARTree's construction kernels at the pages' pruned configuration: gamma = 16
+    draft positions over the vocabulary, K = 64 candidates, width W = 12, beta =
+    -0.2, budget B = 64. The correction head is a trained network outside this
+    library; its log q~ inputs here are fixed seeded values of the right shape
+    (the kernels' work does not depend on them)."""
+
+    GAMMA, K, W, BETA, B = 16, 64, 12, -0.2, 64
+
+    def __init__(self, w, device):
+        import torch
+
+        from gen import tensors as gten
+
+        import draft_tree_verification_dt_amd as dtm
+
+        self.dt, self.torch = dtm, torch
+        g, K, W = self.GAMMA, self.K, self.W
+        self.base = gten.device_logits(g, w.vocab, w.seed, "draft-base")
+        self.ws = torch.empty(max(dtm.dt_topk_rows_workspace_size(g, w.vocab, K), 256), dtype=torch.uint8,
+                              device=device)
+        self.tok = torch.empty((g, K), dtype=torch.int32, device=device)
+        self.lp = torch.empty((g, K), dtype=torch.float32, device=device)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(w.seed)
+        self.logq = torch.log_softmax(torch.randn((g, W, K), generator=gen, device=device) * 2, dim=-1)
+        self.root_score = torch.zeros((1, 1), dtype=torch.float32, device=device)
+        self.par = torch.full((1, g, W), -1, dtype=torch.int32, device=device)
+        self.cand = torch.full((1, g, W), -1, dtype=torch.int32, device=device)
+        self.stok = torch.full((1, g, W), -1, dtype=torch.int32, device=device)
+        self.ssc = torch.full((1, g, W), float("-inf"), dtype=torch.float32, device=device)
+        self.root_tok = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tree = [torch.empty((1, self.B + 1), dtype=dt_, device=device)
+                     for dt_ in (torch.int32, torch.int32, torch.int32, torch.float32)] + \
+                    [torch.empty(1, dtype=torch.int32, device=device)]
+
+    def topk(self):
+        self.dt.dt_topk_rows(self.base, self.K, out_token=self.tok, out_logprob=self.lp, workspace=self.ws)
+
+    def expand(self, d):
+        prev = self.root_score if d == 0 else self.ssc[:, d - 1]
+        lq = self.logq[d:d + 1, :1] if d == 0 else self.logq[d:d + 1]
+        self.dt.dt_expand_depth(prev, lq, self.tok[d:d + 1], self.W, self.BETA,
+                                out=(self.par[:, d], self.cand[:, d], self.stok[:, d], self.ssc[:, d]))
+
+    def prune(self):
+        self.dt.dt_prune_topb(self.par, self.stok, self.ssc, self.root_tok, self.B, out=tuple(self.tree))
+
+    def chain(self):
+        self.topk()
+        for d in range(self.GAMMA):
+            self.expand(d)
+        self.prune()
+
+
+def time_draft_build(rnd, reps=10):
+    db = DraftBuild(rnd.w, rnd.dev)
+    topk_ms = time_on_stream(rnd, lambda i: db.topk(), reps)
+    db.chain()  # every layer filled, so each timed expansion selects from real scores
+    exp_ms = time_on_stream(rnd, lambda i: db.expand(1 + i % (db.GAMMA - 1)), reps)
+    prune_ms = time_on_stream(rnd, lambda i: db.prune(), reps)
+    chain_ms = time_on_stream(rnd, lambda i: db.chain(), reps)
+    n_out = int(db.tree[4].cpu()[0])
+    depth = db.tree[2].cpu().numpy()[0, :n_out]
+    topk_bytes = db.GAMMA * rnd.w.vocab * 4
+    return {"config": f"gamma {db.GAMMA}, vocab {rnd.w.vocab}, K {db.K}, W {db.W}, beta {db.BETA}, B {db.B}",
+            "topk_us": topk_ms * 1e3, "topk_GB/s": topk_bytes / (topk_ms / 1e3) / 1e9,
+            "expand_us": exp_ms * 1e3, "prune_us": prune_ms * 1e3,
+            "chain_us": chain_ms * 1e3, "tree_nodes": n_out, "tree_max_depth": int(depth.max())}
+
+
 def reference_outputs(rnd, t1_offset):
     """One more (untimed) round on candidate table 0 whose outputs the CPU
     baseline leg checks: every layer's attention, the greedy tokens, the walk,
@@ -452,6 +523,7 @@ def main():
     arg_ms = time_argmax_calls(rnd, reps=10)
     smp_ms = time_sample_calls(rnd, reps=10)
     com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
+    draft = time_draft_build(rnd)
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
@@ -479,6 +551,7 @@ def main():
                    "frac_hbm": argmax_bytes / (smp_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "commit": {"kernel": "dt_commit_kv, all layers in one call", "us": com_ms * 1e3, "bytes": com_bytes,
                    "GB/s": com_bytes / (com_ms / 1e3) / 1e9, "accept_len": com_acc.tolist()},
+        "draft_tree": dict(draft, kernels="dt_topk_rows, dt_expand_depth (x16 in the chain), dt_prune_topb"),
         "step_variant": {"temperature": args.temperature, "commit": bool(args.commit)},
         "parity": None,
         "trees": tree_shape(rnd),

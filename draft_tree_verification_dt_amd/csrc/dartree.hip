@@ -72,11 +72,14 @@ __device__ inline uint32_t block_sum_u32(uint32_t v, SelShared& sh) {
   return t;
 }
 
-// The m-th largest key (1 <= m <= number of valid elements) among this block's
-// valid elements, and how many elements equal to it belong to the best m.
+// Keys are never 0 for a candidate (float_key of a finite value, or the bitwise
+// complement of a non-negative index); 0 marks an empty slot.
+
+// The m-th largest key (1 <= m <= number of non-zero keys) among this block's
+// keys, and how many keys equal to it belong to the best m.
 template <int E>
-__device__ void radix_select(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t m, SelShared& sh,
-                             uint32_t& thr, uint32_t& need_eq) {
+__device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh, uint32_t& thr,
+                             uint32_t& need_eq) {
   uint32_t prefix = 0, mask = 0, remaining = m;
   const int lane = threadIdx.x & 63;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -84,7 +87,7 @@ __device__ void radix_select(const uint32_t (&key)[E], const bool (&valid)[E], u
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (valid[e] && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+      if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
     __syncthreads();
     if (threadIdx.x < 64) {
       // lane l holds bins 4l .. 4l+3; find the bin where the count from the top reaches `remaining`
@@ -97,7 +100,7 @@ __device__ void radix_select(const uint32_t (&key)[E], const bool (&valid)[E], u
         const uint32_t o = __shfl_down(incl, off);
         if (lane + off < 64) incl += o;
       }
-      uint32_t cum = incl - s;  // elements in higher bins
+      uint32_t cum = incl - s;  // keys in higher bins
       const uint32_t cs[4] = {c0, c1, c2, c3};
 #pragma unroll
       for (int j = 3; j >= 0; --j) {
@@ -118,50 +121,41 @@ __device__ void radix_select(const uint32_t (&key)[E], const bool (&valid)[E], u
   need_eq = remaining;
 }
 
-// Select the best m valid elements by (key desc, idx asc) and append them,
-// unordered, to out_key/out_idx (LDS or global) through sh.count. Returns the
-// number selected: min(m, valid count). Indices of valid elements are unique.
+// Select the best m candidates (non-zero keys) by (key desc, idx asc) and
+// append them, unordered, to out_key/out_idx (LDS or global) through
+// sh.count. Returns the number selected: min(m, candidates). Indices of the
+// candidates are unique and non-negative.
 template <int E>
-__device__ uint32_t block_select(const uint32_t (&key)[E], const int32_t (&idx)[E], const bool (&valid)[E],
-                                 uint32_t m, SelShared& sh, uint32_t* out_key, int32_t* out_idx) {
+__device__ uint32_t block_select(const uint32_t (&key)[E], const int32_t (&idx)[E], uint32_t m, SelShared& sh,
+                                 uint32_t* out_key, int32_t* out_idx) {
   uint32_t nv = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) nv += valid[e] ? 1u : 0u;
+  for (int e = 0; e < E; ++e) nv += key[e] != 0u ? 1u : 0u;
   const uint32_t total = block_sum_u32(nv, sh);
   const uint32_t take = std::min(m, total);
-  bool sel[E];
-  if (take == total || take == 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) sel[e] = take != 0 && valid[e];
-  } else {
-    uint32_t thr, need_eq;
-    radix_select<E>(key, valid, take, sh, thr, need_eq);
+  if (take == 0) return 0;  // uniform across the block
+  uint32_t thr = 1u, idx_thr = 0xFFFFFFFFu;  // taken: key > thr, or key == thr and idx <= idx_thr
+  if (take < total) {
+    uint32_t need_eq;
+    radix_select<E>(key, take, sh, thr, need_eq);
     uint32_t neq = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == thr) ? 1u : 0u;
+    for (int e = 0; e < E; ++e) neq += key[e] == thr ? 1u : 0u;
     const uint32_t eq_total = block_sum_u32(neq, sh);
-    uint32_t idx_thr = 0xFFFFFFFFu;  // equal elements with idx <= idx_thr are taken
     if (eq_total > need_eq) {
       uint32_t ikey[E];
-      bool iv[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ikey[e] = ~(uint32_t)idx[e];  // the largest ~idx are the smallest idx
-        iv[e] = valid[e] && key[e] == thr;
-      }
+      for (int e = 0; e < E; ++e) ikey[e] = key[e] == thr ? ~(uint32_t)idx[e] : 0u;  // largest ~idx: smallest idx
       uint32_t t2, unused;
-      radix_select<E>(ikey, iv, need_eq, sh, t2, unused);
+      radix_select<E>(ikey, need_eq, sh, t2, unused);
       idx_thr = ~t2;
     }
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      sel[e] = valid[e] && (key[e] > thr || (key[e] == thr && (uint32_t)idx[e] <= idx_thr));
   }
   if (threadIdx.x == 0) sh.count = 0;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    if (sel[e]) {
+    if (key[e] != 0u && (key[e] > thr || (key[e] == thr && (uint32_t)idx[e] <= idx_thr))) {
       const uint32_t pos = atomicAdd(&sh.count, 1u);
       out_key[pos] = key[e];
       out_idx[pos] = idx[e];
@@ -229,7 +223,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   float v[E];
   uint32_t key[E];
   int32_t idx[E];
-  bool valid[E];
+  bool valid[E];  // only for the max and sum below; the selection uses key != 0
   // entry e of thread t: 4 * (t + 256 * (e / 4)) + e % 4 within the chunk (16-byte loads, coalesced)
 #pragma unroll
   for (int q = 0; q < E / 4; ++q) {
@@ -268,11 +262,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = float_key(v[e]);
+  for (int e = 0; e < E; ++e) key[e] = valid[e] ? float_key(v[e]) : 0u;
   __syncthreads();
   const size_t base = ((size_t)row * p.chunks + c) * p.k;
   if (threadIdx.x == 0) p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, (ws[0] + ws[1]) + (ws[2] + ws[3]));
-  const uint32_t got = block_select<E>(key, idx, valid, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base);
+  const uint32_t got = block_select<E>(key, idx, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base);
   for (int j = (int)got + threadIdx.x; j < p.k; j += kSelThreads) {  // a short last chunk: pad
     p.part_key[base + j] = 0u;
     p.part_idx[base + j] = -1;
@@ -280,6 +274,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 }
 
 // grid (rows): merge the chunks' candidates and statistics; k best in order.
+// E candidate slots per thread (E * 256 >= chunks * k).
+template <int E>
 __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   __shared__ SelShared sh;
   __shared__ uint32_t sk[kMaxSortedK];
@@ -307,19 +303,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
-  constexpr int E = kSelPerThread;
   uint32_t key[E];
   int32_t idx[E];
-  bool valid[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = threadIdx.x + kSelThreads * e;
     const bool in = j < M;
-    key[e] = in ? p.part_key[base + j] : 0u;
     idx[e] = in ? p.part_idx[base + j] : -1;
-    valid[e] = in && idx[e] >= 0;
+    key[e] = (in && idx[e] >= 0) ? p.part_key[base + j] : 0u;  // padding of a short chunk: empty
   }
-  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.k, sh, sk, si);
+  const int got = (int)block_select<E>(key, idx, (uint32_t)p.k, sh, sk, si);
   const int n = pow2_at_least(got);
   for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
     sk[j] = 0u;
@@ -350,7 +343,9 @@ struct ExpandParams {
 };
 
 // grid (S): scores of every (parent slot p, candidate c) child, index p * k + c,
-// and the w best by (score desc, index asc), written in that order.
+// and the w best by (score desc, index asc), written in that order. E slots
+// per thread (E * 256 >= w_prev * k).
+template <int E>
 __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams p) {
   __shared__ SelShared sh;
   __shared__ uint32_t sk[kMaxSortedK];
@@ -359,10 +354,8 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
   const float* ps = p.parent_score + s * p.ps_stride;
   const float* lq = p.child_logq + s * p.lq_stride;
   const int M = p.w_prev * p.k;
-  constexpr int E = kSelPerThread;
   uint32_t key[E];
   int32_t idx[E];
-  bool valid[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = threadIdx.x + kSelThreads * e;
@@ -372,11 +365,10 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
       const float a = ps[par] + lq[j];  // Algorithm 1, line 8, in this order
       sc = a + p.beta;
     }
-    key[e] = float_key(sc);
+    key[e] = (j < M && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = j;
-    valid[e] = j < M && isfinite(sc);
   }
-  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.w, sh, sk, si);
+  const int got = (int)block_select<E>(key, idx, (uint32_t)p.w, sh, sk, si);
   const int n = pow2_at_least(got);
   for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
     sk[j] = 0u;
@@ -413,7 +405,8 @@ struct PruneParams {
 
 // grid (S): the best `budget` supertree nodes by (score desc, depth asc, slot
 // asc) -- node index (d - 1) * w + slot orders depth, then slot -- flattened
-// after the root in that order.
+// after the root in that order. E slots per thread (E * 256 >= depths * w).
+template <int E>
 __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p) {
   __shared__ SelShared sh;
   __shared__ uint32_t sk[kMaxSortedK];
@@ -425,22 +418,19 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   const int32_t* spar = p.sel_parent + s * M;
   const int32_t* stok = p.sel_token + s * M;
   const float* ssc = p.sel_score + s * M;
-  constexpr int E = kSelPerThread;
   uint32_t key[E];
   int32_t idx[E];
-  bool valid[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = threadIdx.x + kSelThreads * e;
     const bool in = j < M;
     const float sc = in ? ssc[j] : -INFINITY;
     const int32_t pr = in ? spar[j] : -1;
-    key[e] = float_key(sc);
+    key[e] = (in && pr >= 0 && pr < p.w && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = j;
-    valid[e] = in && pr >= 0 && pr < p.w && isfinite(sc);
   }
   for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
-  const int got = (int)block_select<E>(key, idx, valid, (uint32_t)p.budget, sh, sk, si);
+  const int got = (int)block_select<E>(key, idx, (uint32_t)p.budget, sh, sk, si);
   const int n = pow2_at_least(got);
   for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
     sk[j] = 0u;
@@ -567,7 +557,13 @@ extern "C" int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, in
     hipLaunchKernelGGL(topk_chunks<true>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
   else
     hipLaunchKernelGGL(topk_chunks<false>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
-  hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+  const int64_t M = (int64_t)chunks * k;
+  if (M <= 4 * kSelThreads)
+    hipLaunchKernelGGL(topk_merge<4>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+  else if (M <= 16 * kSelThreads)
+    hipLaunchKernelGGL(topk_merge<16>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_merge<kSelPerThread>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
   return launch_status();
 }
 
@@ -605,8 +601,14 @@ extern "C" int dt_expand_depth(int32_t num_seqs, int32_t w_prev, int32_t k, int3
   p.k = k;
   p.w = w;
   p.beta = beta;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, static_cast<hipStream_t>(stream),
-                     p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t M = (int64_t)w_prev * k;
+  if (M <= 4 * kSelThreads)
+    hipLaunchKernelGGL(expand_kernel<4>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+  else if (M <= 16 * kSelThreads)
+    hipLaunchKernelGGL(expand_kernel<16>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(expand_kernel<kSelPerThread>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
   return launch_status();
 }
 
@@ -637,7 +639,13 @@ extern "C" int dt_prune_topb(int32_t num_seqs, int32_t depths, int32_t w, int32_
   p.depths = depths;
   p.w = w;
   p.budget = budget;
-  hipLaunchKernelGGL(prune_kernel, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, static_cast<hipStream_t>(stream),
-                     p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t M = (int64_t)depths * w;
+  if (M <= 4 * kSelThreads)
+    hipLaunchKernelGGL(prune_kernel<4>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+  else if (M <= 16 * kSelThreads)
+    hipLaunchKernelGGL(prune_kernel<16>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(prune_kernel<kSelPerThread>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
   return launch_status();
 }
