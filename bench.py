@@ -361,7 +361,7 @@ def time_draft_build(rnd, reps=10):
     n_out = int(db.tree[4].cpu()[0])
     depth = db.tree[2].cpu().numpy()[0, :n_out]
     topk_bytes = db.GAMMA * rnd.w.vocab * 4
-    return {"config": f"gamma {db.GAMMA}, vocab {rnd.w.vocab}, K {db.K}, W {db.W}, beta {db.BETA}, B {db.B}",
+    return db, {"config": f"gamma {db.GAMMA}, vocab {rnd.w.vocab}, K {db.K}, W {db.W}, beta {db.BETA}, B {db.B}",
             "topk_us": topk_ms * 1e3, "topk_GB/s": topk_bytes / (topk_ms / 1e3) / 1e9,
             "expand_us": exp_ms * 1e3, "prune_us": prune_ms * 1e3,
             "chain_us": chain_ms * 1e3, "tree_nodes": n_out, "tree_max_depth": int(depth.max())}
@@ -390,7 +390,34 @@ def reference_outputs(rnd, t1_offset):
     return ref
 
 
-def cpu_baseline(rnd, budget_s, ref, t1_offset):
+def draft_oracle(db):
+    """The oracle's DARTree construction over the bench's draft inputs (the same
+    base logits and stand-in log q~), timed, and compared with the GPU's last
+    chain (topk, 16 expansions, prune) node for node."""
+    from oracle import dartree as odt
+
+    torch = db.torch
+    db.chain()
+    torch.cuda.synchronize()
+    base = db.base.cpu().numpy()
+    logq = db.logq.cpu().numpy()
+    t0 = time.perf_counter()
+    ctok, _ = odt.topk_logprobs(base, db.K)
+    heads = [(lambda d: (lambda paths: logq[d][:len(paths)]))(d) for d in range(db.GAMMA)]
+    layers = odt.build_supertree(heads, db.BETA, db.W)
+    kept = odt.prune_topb(layers, db.B)
+    parent, token, depth, _ = odt.tree_arrays(layers, kept, ctok)
+    seconds = time.perf_counter() - t0
+    token[0] = int(db.root_tok.cpu()[0])
+    n = int(db.tree[4].cpu()[0])
+    ok = (np.array_equal(db.tok.cpu().numpy(), ctok) and n == len(kept) and
+          np.array_equal(db.tree[0].cpu().numpy()[0, :n], parent) and
+          np.array_equal(db.tree[1].cpu().numpy()[0, :n], token) and
+          np.array_equal(db.tree[2].cpu().numpy()[0, :n], depth))
+    return seconds, bool(ok)
+
+
+def cpu_baseline(rnd, budget_s, ref, t1_offset, db=None):
     """The oracle, as it is, on this host's cores: a bounded sample of the same
     round (some of the layers' attention, plus argmax, walk and tree build),
     scaled to a full round. Its outputs are compared with the GPU's outputs of
@@ -454,6 +481,11 @@ def cpu_baseline(rnd, budget_s, ref, t1_offset):
     wk, wv = ocommit.commit_kv(f(k0), f(v0), f(rnd.kt[0]), f(rnd.vt[0]), ref["path"], ref["acc"], rnd.offs,
                                w.prefix_lens, rnd.starts)
     commit_ok = bool(np.array_equal(wk, f(k1)) and np.array_equal(wv, f(v1)))
+    k0h, v0h, kth, vth = f(k0), f(v0), f(rnd.kt[0]), f(rnd.vt[0])
+    t0 = time.perf_counter()
+    ocommit.commit_kv(k0h, v0h, kth, vth, ref["path"], ref["acc"], rnd.offs, w.prefix_lens, rnd.starts)
+    t_commit = (time.perf_counter() - t0) * w.layers  # one layer timed, scaled to all layers
+    t_draft, draft_ok = draft_oracle(db) if db is not None else (None, None)
     round_s = t_build + np.mean(layer_times) * w.layers + t_arg + t_walk
     flops = rnd.attention_flops(t) * w.layers
     parity = {"layers_checked": len(layer_times), "attention_max_abs_err": worst_abs,
@@ -462,7 +494,8 @@ def cpu_baseline(rnd, budget_s, ref, t1_offset):
               "argmax_exact": bool(np.array_equal(ref["am"], am)), "walk_exact": bool(walk_ok),
               "sample_t1_ok": sample_ok, "sample_t1_rows_checked": int(len(ids)),
               "sample_t1_exact_rows": int((gpu == smp).sum()),
-              "commit_exact": commit_ok, "mean_accept_len": float(np.mean([L for _, L, _ in walks]))}
+              "commit_exact": commit_ok, "draft_tree_exact": draft_ok,
+              "mean_accept_len": float(np.mean([L for _, L, _ in walks]))}
     return {
         "value": flops / round_s / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas_threads) if blas_threads else cores),
         "kind": "oracle",
@@ -470,7 +503,8 @@ def cpu_baseline(rnd, budget_s, ref, t1_offset):
                   f"plus tree build, argmax and walk once; scaled to one full round",
         "us_per_round": round_s * 1e6, "host_cores_visible": cores, "blas_threads": blas_threads,
         "seconds": {"build": t_build, "attention_per_layer": float(np.mean(layer_times)), "argmax": t_arg,
-                    "walk": t_walk, "sample_t1": t_smp},
+                    "walk": t_walk, "sample_t1": t_smp, "commit_all_layers": t_commit,
+                    "draft_tree_construction": t_draft},
     }, parity
 
 
@@ -523,7 +557,7 @@ def main():
     arg_ms = time_argmax_calls(rnd, reps=10)
     smp_ms = time_sample_calls(rnd, reps=10)
     com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
-    draft = time_draft_build(rnd)
+    db, draft = time_draft_build(rnd)
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
@@ -559,7 +593,7 @@ def main():
     if not args.no_cpu_baseline:
         t1_offset = 424242
         ref = reference_outputs(rnd, t1_offset)
-        rec["cpu_baseline"], rec["parity"] = cpu_baseline(rnd, args.cpu_budget_s, ref, t1_offset)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(rnd, args.cpu_budget_s, ref, t1_offset, db)
     print(json.dumps(rec), flush=True)
 
 

@@ -55,63 +55,60 @@ __device__ inline float key_float(uint32_t k) {
 struct SelShared {
   uint32_t hist[256];
   uint32_t red[kSelThreads / 64];
-  uint32_t bin;
-  uint32_t remaining;
+  uint32_t bin, remaining, in_bin, total;
   uint32_t count;
 };
-
-__device__ inline uint32_t block_sum_u32(uint32_t v, SelShared& sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) t += sh.red[w];
-  return t;
-}
 
 // Keys are never 0 for a candidate (float_key of a finite value, or the bitwise
 // complement of a non-negative index); 0 marks an empty slot.
 
-// The m-th largest key (1 <= m <= number of non-zero keys) among this block's
-// keys, and how many keys equal to it belong to the best m.
+// Histogram of digit (key >> shift) & 255 over the keys whose bits above the
+// digit equal `prefix` (mask selects them); then wave 0 finds, counting from the
+// top bin down, the bin holding the `remaining`-th key, and publishes it with
+// the count of keys above it, its own count and the total.
 template <int E>
-__device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh, uint32_t& thr,
-                             uint32_t& need_eq) {
-  uint32_t prefix = 0, mask = 0, remaining = m;
-  const int lane = threadIdx.x & 63;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[threadIdx.x] = 0;  // 256 threads, 256 bins
-    __syncthreads();
+__device__ void digit_pass(const uint32_t (&key)[E], uint32_t prefix, uint32_t mask, int shift, uint32_t remaining,
+                           SelShared& sh) {
+  sh.hist[threadIdx.x] = 0;  // 256 threads, 256 bins
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l holds bins 4l .. 4l+3; find the bin where the count from the top reaches `remaining`
-      const uint32_t c0 = sh.hist[4 * lane], c1 = sh.hist[4 * lane + 1], c2 = sh.hist[4 * lane + 2],
-                     c3 = sh.hist[4 * lane + 3];
-      const uint32_t s = c0 + c1 + c2 + c3;
-      uint32_t incl = s;  // sum over lanes >= this one
+  for (int e = 0; e < E; ++e)
+    if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint32_t c0 = sh.hist[4 * lane], c1 = sh.hist[4 * lane + 1], c2 = sh.hist[4 * lane + 2],
+                   c3 = sh.hist[4 * lane + 3];
+    const uint32_t s = c0 + c1 + c2 + c3;
+    uint32_t incl = s;  // keys in this lane's bins and above
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(incl, off);
-        if (lane + off < 64) incl += o;
-      }
-      uint32_t cum = incl - s;  // keys in higher bins
-      const uint32_t cs[4] = {c0, c1, c2, c3};
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (cum < remaining && cum + cs[j] >= remaining) {
-          sh.bin = 4 * lane + j;
-          sh.remaining = remaining - cum;
-        }
-        cum += cs[j];
-      }
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(incl, off);
+      if (lane + off < 64) incl += o;
     }
-    __syncthreads();
+    if (lane == 0) sh.total = incl;
+    uint32_t cum = incl - s;  // keys in higher bins
+    const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (cum < remaining && cum + cs[j] >= remaining) {
+        sh.bin = 4 * lane + j;
+        sh.remaining = remaining - cum;
+        sh.in_bin = cs[j];
+      }
+      cum += cs[j];
+    }
+  }
+  __syncthreads();
+}
+
+// The m-th largest key (1 <= m <= number of non-zero keys) and how many keys
+// equal to it belong to the best m (used for index tie-breaks only).
+template <int E>
+__device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh, uint32_t& thr, uint32_t& need_eq) {
+  uint32_t prefix = 0, mask = 0, remaining = m;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    digit_pass<E>(key, prefix, mask, shift, remaining, sh);
     prefix |= sh.bin << shift;
     mask |= 0xFFu << shift;
     remaining = sh.remaining;
@@ -122,44 +119,65 @@ __device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh
 }
 
 // Select the best m candidates (non-zero keys) by (key desc, idx asc) and
-// append them, unordered, to out_key/out_idx (LDS or global) through
-// sh.count. Returns the number selected: min(m, candidates). Indices of the
-// candidates are unique and non-negative.
-template <int E>
-__device__ uint32_t block_select(const uint32_t (&key)[E], const int32_t (&idx)[E], uint32_t m, SelShared& sh,
-                                 uint32_t* out_key, int32_t* out_idx) {
-  uint32_t nv = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) nv += key[e] != 0u ? 1u : 0u;
-  const uint32_t total = block_sum_u32(nv, sh);
-  const uint32_t take = std::min(m, total);
-  if (take == 0) return 0;  // uniform across the block
-  uint32_t thr = 1u, idx_thr = 0xFFFFFFFFu;  // taken: key > thr, or key == thr and idx <= idx_thr
-  if (take < total) {
-    uint32_t need_eq;
-    radix_select<E>(key, take, sh, thr, need_eq);
-    uint32_t neq = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) neq += key[e] == thr ? 1u : 0u;
-    const uint32_t eq_total = block_sum_u32(neq, sh);
-    if (eq_total > need_eq) {
+// append them with their two payload words, unordered, to the LDS arrays
+// through sh.count. Returns the number selected: min(m, candidates), uniform
+// across the block. Candidate indices are unique and non-negative.
+//
+// The first digit pass also counts the candidates. A pass whose chosen bin is
+// taken whole (its count equals what is still needed) ends the search: every
+// key at or above that bin's lowest value is in. Only when the last digit
+// leaves a tie does a second radix select over the tied indices run.
+template <int E, bool PAY>
+__device__ uint32_t select_best(const uint32_t (&key)[E], const int32_t (&idx)[E], const int32_t (&p0)[E],
+                                const int32_t (&p1)[E], uint32_t m, SelShared& sh, uint32_t* out_key, int32_t* out_idx,
+                                int32_t* out_p0, int32_t* out_p1) {
+  if (m == 0) return 0;
+  uint32_t prefix = 0, mask = 0, remaining = m;
+  uint32_t lo = 1;                                      // mode A: take every key >= lo
+  bool tie = false;                                     // mode B: key > prefix, or == prefix and idx <= idx_thr
+  uint32_t idx_thr = 0xFFFFFFFFu, take = m;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    digit_pass<E>(key, prefix, mask, shift, remaining, sh);
+    const uint32_t total = sh.total, bin = sh.bin, rem = sh.remaining, in_bin = sh.in_bin;
+    __syncthreads();
+    if (shift == 24 && total <= m) {  // everything is taken
+      take = total;
+      break;
+    }
+    prefix |= bin << shift;
+    mask |= 0xFFu << shift;
+    if (in_bin == rem) {  // the whole bin is in
+      lo = prefix;
+      break;
+    }
+    remaining = rem;
+    if (shift == 0) {  // a tie at one key value: the lowest indices among it
+      tie = true;
       uint32_t ikey[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) ikey[e] = key[e] == thr ? ~(uint32_t)idx[e] : 0u;  // largest ~idx: smallest idx
+      for (int e = 0; e < E; ++e) ikey[e] = key[e] == prefix ? ~(uint32_t)idx[e] : 0u;  // largest ~idx first
       uint32_t t2, unused;
-      radix_select<E>(ikey, need_eq, sh, t2, unused);
+      radix_select<E>(ikey, remaining, sh, t2, unused);
       idx_thr = ~t2;
     }
   }
+  if (take == 0) return 0;
   if (threadIdx.x == 0) sh.count = 0;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] != 0u && (key[e] > thr || (key[e] == thr && (uint32_t)idx[e] <= idx_thr))) {
+  for (int e = 0; e < E; ++e) {
+    const bool in = key[e] != 0u &&
+                    (tie ? (key[e] > prefix || (key[e] == prefix && (uint32_t)idx[e] <= idx_thr)) : key[e] >= lo);
+    if (in) {
       const uint32_t pos = atomicAdd(&sh.count, 1u);
       out_key[pos] = key[e];
       out_idx[pos] = idx[e];
+      if (PAY) {
+        out_p0[pos] = p0[e];
+        out_p1[pos] = p1[e];
+      }
     }
+  }
   __syncthreads();
   return take;
 }
@@ -169,22 +187,53 @@ __device__ inline bool ahead(uint32_t ka, int32_t ia, uint32_t kb, int32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// Sort n (a power of two, <= kMaxSortedK) LDS entries best first.
-__device__ void bitonic_sort(uint32_t* k, int32_t* ix, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
+__device__ inline int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Order of the n (<= kMaxSortedK) selected entries: ord[r] = the LDS position of
+// the r-th best; sk and si are left as they are. Up to 256 entries every thread
+// ranks one entry against all of them (no barriers inside the loop); more are
+// sorted by a bitonic network over copies (tk, ti) that carries the positions.
+__device__ void order_selected(const uint32_t* sk, const int32_t* si, int n, int32_t* ord, uint32_t* tk,
+                               int32_t* ti) {
+  if (n <= kSelThreads) {
+    const int j = threadIdx.x;
+    if (j < n) {
+      const uint32_t kj = sk[j];
+      const int32_t ij = si[j];
+      int r = 0;
+      for (int t = 0; t < n; ++t) r += ahead(sk[t], si[t], kj, ij) ? 1 : 0;
+      ord[r] = j;
+    }
+    __syncthreads();
+    return;
+  }
+  const int np = pow2_at_least(n);  // padding sorts behind every real entry
+  for (int j = threadIdx.x; j < np; j += kSelThreads) {
+    tk[j] = j < n ? sk[j] : 0u;
+    ti[j] = j < n ? si[j] : INT_MAX;
+    ord[j] = j;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += kSelThreads) {
+      for (int i = threadIdx.x; i < np / 2; i += kSelThreads) {
         const int a = 2 * i - (i & (stride - 1));
         const int b = a + stride;
         const bool best_first = (a & size) == 0;
-        const bool b_ahead = ahead(k[b], ix[b], k[a], ix[a]);
-        if (b_ahead == best_first) {
-          const uint32_t tk = k[a];
-          k[a] = k[b];
-          k[b] = tk;
-          const int32_t ti = ix[a];
-          ix[a] = ix[b];
-          ix[b] = ti;
+        if (ahead(tk[b], ti[b], tk[a], ti[a]) == best_first) {
+          const uint32_t x = tk[a];
+          tk[a] = tk[b];
+          tk[b] = x;
+          const int32_t y = ti[a];
+          ti[a] = ti[b];
+          ti[b] = y;
+          const int32_t z = ord[a];
+          ord[a] = ord[b];
+          ord[b] = z;
         }
       }
       __syncthreads();
@@ -192,11 +241,16 @@ __device__ void bitonic_sort(uint32_t* k, int32_t* ix, int n) {
   }
 }
 
-__device__ inline int pow2_at_least(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
+// LDS of the selecting kernels: the selected entries, their order and scratch.
+struct SelLds {
+  uint32_t key[kMaxSortedK];
+  int32_t idx[kMaxSortedK];
+  int32_t p0[kMaxSortedK];
+  int32_t p1[kMaxSortedK];
+  int32_t ord[kMaxSortedK];
+  uint32_t tk[kMaxSortedK];
+  int32_t ti[kMaxSortedK];
+};
 
 // ---------------------------------------------------------------- top-K of rows
 
@@ -266,7 +320,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   __syncthreads();
   const size_t base = ((size_t)row * p.chunks + c) * p.k;
   if (threadIdx.x == 0) p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, (ws[0] + ws[1]) + (ws[2] + ws[3]));
-  const uint32_t got = block_select<E>(key, idx, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base);
+  const uint32_t got =
+      select_best<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base, nullptr, nullptr);
   for (int j = (int)got + threadIdx.x; j < p.k; j += kSelThreads) {  // a short last chunk: pad
     p.part_key[base + j] = 0u;
     p.part_idx[base + j] = -1;
@@ -278,8 +333,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   __shared__ SelShared sh;
-  __shared__ uint32_t sk[kMaxSortedK];
-  __shared__ int32_t si[kMaxSortedK];
+  __shared__ SelLds L;
   __shared__ float red[kSelThreads / 64];
   const int64_t row = blockIdx.x;
   const int M = p.chunks * p.k;
@@ -312,18 +366,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
     idx[e] = in ? p.part_idx[base + j] : -1;
     key[e] = (in && idx[e] >= 0) ? p.part_key[base + j] : 0u;  // padding of a short chunk: empty
   }
-  const int got = (int)block_select<E>(key, idx, (uint32_t)p.k, sh, sk, si);
-  const int n = pow2_at_least(got);
-  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
-    sk[j] = 0u;
-    si[j] = INT_MAX;
-  }
-  __syncthreads();
-  bitonic_sort(sk, si, n);
-  for (int j = threadIdx.x; j < p.k; j += kSelThreads) {
-    const bool ok = j < got;
-    p.out_token[row * p.k + j] = ok ? si[j] : -1;
-    p.out_logprob[row * p.k + j] = ok ? key_float(sk[j]) - lse : -INFINITY;
+  const int got = (int)select_best<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L.key, L.idx, nullptr, nullptr);
+  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
+    const bool ok = r < got;
+    const int j = ok ? L.ord[r] : 0;
+    p.out_token[row * p.k + r] = ok ? L.idx[j] : -1;
+    p.out_logprob[row * p.k + r] = ok ? key_float(L.key[j]) - lse : -INFINITY;
   }
 }
 
@@ -348,43 +397,39 @@ struct ExpandParams {
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams p) {
   __shared__ SelShared sh;
-  __shared__ uint32_t sk[kMaxSortedK];
-  __shared__ int32_t si[kMaxSortedK];
+  __shared__ SelLds L;
   const int64_t s = blockIdx.x;
   const float* ps = p.parent_score + s * p.ps_stride;
   const float* lq = p.child_logq + s * p.lq_stride;
+  const int32_t* ct = p.cand_token + s * p.ct_stride;
   const int M = p.w_prev * p.k;
   uint32_t key[E];
-  int32_t idx[E];
+  int32_t idx[E], tok[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = threadIdx.x + kSelThreads * e;
     float sc = -INFINITY;
+    tok[e] = -1;
     if (j < M) {
       const int par = j / p.k;
       const float a = ps[par] + lq[j];  // Algorithm 1, line 8, in this order
       sc = a + p.beta;
+      tok[e] = ct[j - par * p.k];
     }
     key[e] = (j < M && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = j;
   }
-  const int got = (int)block_select<E>(key, idx, (uint32_t)p.w, sh, sk, si);
-  const int n = pow2_at_least(got);
-  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
-    sk[j] = 0u;
-    si[j] = INT_MAX;
-  }
-  __syncthreads();
-  bitonic_sort(sk, si, n);
+  const int got = (int)select_best<E, true>(key, idx, tok, tok, (uint32_t)p.w, sh, L.key, L.idx, L.p0, L.p1);
+  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
   const int64_t o = s * p.out_stride;
-  for (int j = threadIdx.x; j < p.w; j += kSelThreads) {
-    const bool ok = j < got;
-    const int child = ok ? si[j] : 0;
-    const int c = child % p.k;
-    p.sel_parent[o + j] = ok ? child / p.k : -1;
-    p.sel_cand[o + j] = ok ? c : -1;
-    p.sel_token[o + j] = ok ? p.cand_token[s * p.ct_stride + c] : -1;
-    p.sel_score[o + j] = ok ? key_float(sk[j]) : -INFINITY;
+  for (int r = threadIdx.x; r < p.w; r += kSelThreads) {
+    const bool ok = r < got;
+    const int j = ok ? L.ord[r] : 0;
+    const int child = ok ? L.idx[j] : 0;
+    p.sel_parent[o + r] = ok ? child / p.k : -1;
+    p.sel_cand[o + r] = ok ? child % p.k : -1;
+    p.sel_token[o + r] = ok ? L.p0[j] : -1;
+    p.sel_score[o + r] = ok ? key_float(L.key[j]) : -INFINITY;
   }
 }
 
@@ -409,8 +454,7 @@ struct PruneParams {
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p) {
   __shared__ SelShared sh;
-  __shared__ uint32_t sk[kMaxSortedK];
-  __shared__ int32_t si[kMaxSortedK];
+  __shared__ SelLds L;
   __shared__ int16_t newpos[kSelMaxCand];  // supertree node -> row in the output (-1: not kept)
   __shared__ int bad;
   const int64_t s = blockIdx.x;
@@ -419,36 +463,32 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   const int32_t* stok = p.sel_token + s * M;
   const float* ssc = p.sel_score + s * M;
   uint32_t key[E];
-  int32_t idx[E];
+  int32_t idx[E], tok[E], par[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = threadIdx.x + kSelThreads * e;
     const bool in = j < M;
     const float sc = in ? ssc[j] : -INFINITY;
-    const int32_t pr = in ? spar[j] : -1;
-    key[e] = (in && pr >= 0 && pr < p.w && isfinite(sc)) ? float_key(sc) : 0u;
+    par[e] = in ? spar[j] : -1;
+    tok[e] = in ? stok[j] : -1;
+    key[e] = (in && par[e] >= 0 && par[e] < p.w && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = j;
   }
   for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
-  const int got = (int)block_select<E>(key, idx, (uint32_t)p.budget, sh, sk, si);
-  const int n = pow2_at_least(got);
-  for (int j = got + threadIdx.x; j < n; j += kSelThreads) {
-    sk[j] = 0u;
-    si[j] = INT_MAX;
-  }
   if (threadIdx.x == 0) bad = 0;
-  __syncthreads();
-  bitonic_sort(sk, si, n);
-  for (int j = threadIdx.x; j < got; j += kSelThreads) newpos[si[j]] = (int16_t)(j + 1);
+  const int got = (int)select_best<E, true>(key, idx, tok, par, (uint32_t)p.budget, sh, L.key, L.idx, L.p0, L.p1);
+  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  for (int r = threadIdx.x; r < got; r += kSelThreads) newpos[L.idx[L.ord[r]]] = (int16_t)(r + 1);
   __syncthreads();
   // With beta <= 0 and log-probabilities <= 0 a child never precedes its parent
-  // (Lemma 1); check it, and keep only nodes whose parent is kept before them if not.
-  for (int j = threadIdx.x; j < got; j += kSelThreads) {
-    const int node = si[j];
-    const int d = node / p.w + 1;
-    if (d > 1) {
-      const int pp = newpos[(d - 2) * p.w + spar[node]];
-      if (pp < 0 || pp > j) bad = 1;
+  // (Lemma 1); check it, and if the data break it keep only nodes whose parent
+  // is kept before them.
+  for (int r = threadIdx.x; r < got; r += kSelThreads) {
+    const int j = L.ord[r];
+    const int node = L.idx[j];
+    if (node >= p.w) {  // depth > 1
+      const int pp = newpos[node - p.w - node % p.w + L.p1[j]];
+      if (pp < 1 || pp > r) bad = 1;
     }
   }
   __syncthreads();
@@ -457,12 +497,12 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
     if (threadIdx.x == 0) {
       for (int j = 0; j < M; ++j) newpos[j] = -1;
       int cnt = 0;
-      for (int j = 0; j < got; ++j) {
-        const int node = si[j];
-        const int d = node / p.w + 1;
-        const int pp = d > 1 ? newpos[(d - 2) * p.w + spar[node]] : 0;
+      for (int r = 0; r < got; ++r) {
+        const int j = L.ord[r];
+        const int node = L.idx[j];
+        const int pp = node >= p.w ? newpos[node - p.w - node % p.w + L.p1[j]] : 0;
         if (pp >= 0) {
-          si[cnt] = node;
+          L.ord[cnt] = j;
           newpos[node] = (int16_t)(cnt + 1);
           ++cnt;
         }
@@ -480,20 +520,20 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
     p.score[o] = 0.f;
     p.n_out[s] = kept + 1;
   }
-  for (int j = threadIdx.x; j < p.budget; j += kSelThreads) {
-    const int64_t r = o + 1 + j;
-    if (j < kept) {
-      const int node = si[j];
-      const int d = node / p.w + 1;
-      p.parent[r] = d > 1 ? newpos[(d - 2) * p.w + spar[node]] : 0;
-      p.token[r] = stok[node];
-      p.depth[r] = d;
-      p.score[r] = ssc[node];
+  for (int r = threadIdx.x; r < p.budget; r += kSelThreads) {
+    const int64_t row = o + 1 + r;
+    if (r < kept) {
+      const int j = L.ord[r];
+      const int node = L.idx[j];
+      p.parent[row] = node >= p.w ? newpos[node - p.w - node % p.w + L.p1[j]] : 0;
+      p.token[row] = L.p0[j];
+      p.depth[row] = node / p.w + 1;
+      p.score[row] = key_float(L.key[j]);
     } else {
-      p.parent[r] = -1;
-      p.token[r] = -1;
-      p.depth[r] = -1;
-      p.score[r] = -INFINITY;
+      p.parent[row] = -1;
+      p.token[row] = -1;
+      p.depth[row] = -1;
+      p.score[row] = -INFINITY;
     }
   }
 }
