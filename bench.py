@@ -358,13 +358,20 @@ def time_draft_build(rnd, reps=10):
     exp_ms = time_on_stream(rnd, lambda i: db.expand(1 + i % (db.GAMMA - 1)), reps)
     prune_ms = time_on_stream(rnd, lambda i: db.prune(), reps)
     chain_ms = time_on_stream(rnd, lambda i: db.chain(), reps)
+    # the same chain from one HIP graph: no host launch gaps between its 18 kernels
+    torch = rnd.torch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        db.chain()
+    graph_ms = time_on_stream(rnd, lambda i: graph.replay(), reps)
     n_out = int(db.tree[4].cpu()[0])
     depth = db.tree[2].cpu().numpy()[0, :n_out]
     topk_bytes = db.GAMMA * rnd.w.vocab * 4
     return db, {"config": f"gamma {db.GAMMA}, vocab {rnd.w.vocab}, K {db.K}, W {db.W}, beta {db.BETA}, B {db.B}",
             "topk_us": topk_ms * 1e3, "topk_GB/s": topk_bytes / (topk_ms / 1e3) / 1e9,
             "expand_us": exp_ms * 1e3, "prune_us": prune_ms * 1e3,
-            "chain_us": chain_ms * 1e3, "tree_nodes": n_out, "tree_max_depth": int(depth.max())}
+            "chain_us": chain_ms * 1e3, "chain_graph_us": graph_ms * 1e3, "tree_nodes": n_out,
+            "tree_max_depth": int(depth.max())}
 
 
 def reference_outputs(rnd, t1_offset):

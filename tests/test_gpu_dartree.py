@@ -278,3 +278,62 @@ def test_factorised_head_equals_host_heap():
             assert list(gd.cpu().numpy()[0, :m]) == list(hd)
             np.testing.assert_array_equal(gs.cpu().numpy()[0, :m].astype(np.float64), hs)
     assert ran >= 3
+
+
+def test_construction_replays_from_a_hip_graph():
+    """The whole construction (top-K, sixteen expansions, pruning) captured once
+    in a HIP graph and replayed: every replay, with new inputs written into the
+    same buffers between replays, equals the eager calls on those inputs."""
+    import torch
+
+    require_gpu()
+    S, gamma, V, K, W, B, beta = 2, 16, 151936, 64, 12, 64, -0.2
+    r = grng.stream(3, "graph")
+    dev = "cuda"
+    base = torch.empty((S * gamma, V), dtype=torch.float32, device=dev)
+    logq = torch.empty((S, gamma, W, K), dtype=torch.float32, device=dev)
+    roots = dev_i32(r.integers(0, V, size=S))
+    ws = torch.empty(dt.dt_topk_rows_workspace_size(S * gamma, V, K), dtype=torch.uint8, device=dev)
+    tok = torch.empty((S * gamma, K), dtype=torch.int32, device=dev)
+    lp = torch.empty((S * gamma, K), dtype=torch.float32, device=dev)
+    sup = [torch.empty((S, gamma, W), dtype=t, device=dev) for t in (torch.int32, torch.int32, torch.int32, torch.float32)]
+    root_score = torch.zeros((S, 1), dtype=torch.float32, device=dev)
+    out = [torch.empty((S, B + 1), dtype=t, device=dev) for t in (torch.int32, torch.int32, torch.int32, torch.float32)]
+    n_out = torch.empty(S, dtype=torch.int32, device=dev)
+
+    def chain():
+        dt.dt_topk_rows(base, K, out_token=tok, out_logprob=lp, workspace=ws)
+        ctok = tok.view(S, gamma, K)
+        for d in range(gamma):
+            prev = root_score if d == 0 else sup[3][:, d - 1]
+            lq = logq[:, 0, :1] if d == 0 else logq[:, d]
+            dt.dt_expand_depth(prev, lq, ctok[:, d], W, beta, out=tuple(x[:, d] for x in sup))
+        dt.dt_prune_topb(sup[0], sup[2], sup[3], roots, B, out=(*out, n_out))
+
+    def fill(seed):
+        g = np.random.default_rng(seed)
+        base.copy_(torch.from_numpy((g.standard_normal((S * gamma, V)) * 3).astype(np.float32)))
+        logq.copy_(torch.log_softmax(torch.from_numpy(g.standard_normal((S, gamma, W, K)).astype(np.float32)), -1))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [x.cpu().clone() for x in (*out, n_out)]
+
+    fill(0)
+    chain()  # warm-up: loads the code objects and caches the device properties before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    print("dartree construction captured", flush=True)
+    for rep, seed in enumerate([1, 2, 3]):
+        fill(seed)
+        chain()
+        eager = snapshot()
+        for x in (*out, n_out):
+            x.fill_(-7)
+        graph.replay()
+        replayed = snapshot()
+        for a, b in zip(eager, replayed):
+            assert torch.equal(a, b), f"replay {rep}"
+        assert int(replayed[4][0]) == B + 1
