@@ -106,8 +106,8 @@ class Round:
         self.bonus = torch.empty(S, dtype=torch.int32, device=device)
         ws_att = dt.dt_tree_attention_workspace_size(self.q[0], self.kt[0], self.kp[0], self.layout)
         self.ws_att = torch.empty(max(ws_att, 256), dtype=torch.uint8, device=device)
-        ws_am = dt.dt_argmax_rows_workspace_size(N, w.vocab)
-        self.ws_am = torch.empty(max(ws_am, 256), dtype=torch.uint8, device=device)
+        ws_am = max(dt.dt_argmax_rows_workspace_size(N, w.vocab), dt.dt_sample_rows_workspace_size(N, w.vocab))
+        self.ws_am = torch.empty(max(ws_am, 256), dtype=torch.uint8, device=device)  # greedy and sampled scans
         self.upload_done = [None, None]
         self.commit_args = dt.CommitArgs(self.layout, np.asarray(w.prefix_lens) + np.asarray(w.nodes), self.kt,
                                          self.vt, self.kp, self.vp, max_path=w.depths + 1)

@@ -116,9 +116,10 @@ __device__ inline void wave_reduce(float& bv, int& bi) {
   }
 }
 
+template <int THREADS>
 __device__ inline void block_reduce(float& bv, int& bi) {
-  __shared__ float sv[kThreads / 64];
-  __shared__ int si[kThreads / 64];
+  __shared__ float sv[THREADS / 64];
+  __shared__ int si[THREADS / 64];
   wave_reduce(bv, bi);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
@@ -127,7 +128,7 @@ __device__ inline void block_reduce(float& bv, int& bi) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 1; k < kThreads / 64; ++k)
+    for (int k = 1; k < THREADS / 64; ++k)
       if (better(sv[k], si[k], bv, bi)) {
         bv = sv[k];
         bi = si[k];
@@ -158,9 +159,9 @@ __device__ inline f32x4 gumbel4(f32x4 v, uint32_t row, uint32_t j, const Gumbel&
 }
 
 // grid: (chunks, rows). VEC: row starts are 16-byte aligned. SAMPLE: compare
-// Gumbel scores instead of logits.
-template <bool VEC, bool SAMPLE>
-__global__ __launch_bounds__(kThreads) void argmax_chunks(const float* __restrict__ x, int64_t vocab, int64_t stride,
+// Gumbel scores instead of logits. THREADS x UNROLL 16-byte loads in flight.
+template <bool VEC, bool SAMPLE, int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void argmax_chunks(const float* __restrict__ x, int64_t vocab, int64_t stride,
                                                           int64_t chunk_len, int chunks, int32_t* __restrict__ out_idx,
                                                           float2* __restrict__ part, const Gumbel g) {
   const int64_t row = blockIdx.y;
@@ -174,21 +175,21 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const float* __restric
     const int64_t beg4 = beg >> 2, end4 = end >> 2;  // full float4s; beg is a multiple of 4
     const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
     int64_t j = beg4 + threadIdx.x;
-    for (; j + (kUnroll - 1) * kThreads < end4; j += kUnroll * kThreads) {
-      f32x4 v[kUnroll];
+    for (; j + (UNROLL - 1) * THREADS < end4; j += UNROLL * THREADS) {
+      f32x4 v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(x4 + j + u * kThreads);
+      for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(x4 + j + u * THREADS);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int base = (int)((j + u * kThreads) << 2);
-        if (SAMPLE) v[u] = gumbel4(v[u], (uint32_t)row, (uint32_t)(j + u * kThreads), g);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int base = (int)((j + u * THREADS) << 2);
+        if (SAMPLE) v[u] = gumbel4(v[u], (uint32_t)row, (uint32_t)(j + u * THREADS), g);
         TAKE_IF_LARGER(v[u].x, base);
         TAKE_IF_LARGER(v[u].y, base + 1);
         TAKE_IF_LARGER(v[u].z, base + 2);
         TAKE_IF_LARGER(v[u].w, base + 3);
       }
     }
-    for (; j < end4; j += kThreads) {
+    for (; j < end4; j += THREADS) {
       f32x4 v = __builtin_nontemporal_load(x4 + j);
       const int base = (int)(j << 2);
       if (SAMPLE) v = gumbel4(v, (uint32_t)row, (uint32_t)j, g);
@@ -197,17 +198,17 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const float* __restric
       TAKE_IF_LARGER(v.z, base + 2);
       TAKE_IF_LARGER(v.w, base + 3);
     }
-    for (int64_t t = (end4 << 2) + threadIdx.x; t < end; t += kThreads) {
+    for (int64_t t = (end4 << 2) + threadIdx.x; t < end; t += THREADS) {
       const float v = entry_value<SAMPLE>(xr[t], t, (uint32_t)row, g);
       TAKE_IF_LARGER(v, (int)t);
     }
   } else {
-    for (int64_t t = beg + threadIdx.x; t < end; t += kThreads) {
+    for (int64_t t = beg + threadIdx.x; t < end; t += THREADS) {
       const float v = entry_value<SAMPLE>(xr[t], t, (uint32_t)row, g);
       TAKE_IF_LARGER(v, (int)t);
     }
   }
-  block_reduce(bv, bi);
+  block_reduce<THREADS>(bv, bi);
   if (threadIdx.x == 0) {
     if (chunks == 1) {
       out_idx[row] = (bi >= 0 && bi < vocab) ? bi : 0;  // bi stays unset only when no entry exceeds -inf (all -inf, or NaN): index 0
@@ -237,7 +238,21 @@ __global__ __launch_bounds__(256) void argmax_merge(int64_t rows, int64_t vocab,
   if (lane == 0) out_idx[row] = (bi >= 0 && bi < vocab) ? bi : 0;
 }
 
-int plan_chunks(int64_t rows, int64_t vocab, int cus, int64_t* chunk_len, int* chunks) {
+// Greedy scans of at least one row per CU take one 512-thread workgroup per row
+// (8 loads in flight per thread, 64 KB per workgroup: with a workgroup on every
+// CU that is about what HBM needs in flight), so no merge kernel runs. The
+// sampling scan keeps more, smaller workgroups per CU, which its Philox
+// arithmetic needs to overlap with the loads. Fewer rows are cut into chunks of
+// 256-thread workgroups and merged.
+constexpr int kWideThreads = 512;
+constexpr int kWideUnroll = 8;
+
+int plan_chunks(int64_t rows, int64_t vocab, int cus, bool sample, int64_t* chunk_len, int* chunks) {
+  if (!sample && rows >= cus) {
+    *chunk_len = vocab;
+    *chunks = 1;
+    return DT_OK;
+  }
   // enough workgroups to cover the CUs several times over, chunks >= 8K entries
   const int64_t target_wg = 8LL * cus;
   int64_t c = rows >= target_wg ? 1 : ceil_div(target_wg, std::max<int64_t>(rows, 1));
@@ -253,18 +268,28 @@ int plan_chunks(int64_t rows, int64_t vocab, int cus, int64_t* chunk_len, int* c
 }  // namespace
 }  // namespace dt
 
-extern "C" int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
+namespace dt {
+namespace {
+
+int scan_workspace_size(int64_t rows, int64_t vocab, bool sample, size_t* bytes) {
   if (!bytes) return DT_ERR_NULL;
   if (rows < 0 || vocab < 1 || vocab > INT_MAX) return DT_ERR_SHAPE;
   int cus = 0;
-  int st = dt::current_device_cus(&cus);
+  int st = current_device_cus(&cus);
   if (st != DT_OK) return st;
   int64_t len;
   int chunks;
-  st = dt::plan_chunks(rows, vocab, cus, &len, &chunks);
+  st = plan_chunks(rows, vocab, cus, sample, &len, &chunks);
   if (st != DT_OK) return st;
-  *bytes = chunks > 1 ? dt::round_up((size_t)rows * chunks * sizeof(float2), 256) : 0;
+  *bytes = chunks > 1 ? round_up((size_t)rows * chunks * sizeof(float2), 256) : 0;
   return DT_OK;
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
+  return dt::scan_workspace_size(rows, vocab, false, bytes);
 }
 
 namespace dt {
@@ -277,7 +302,7 @@ int launch_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_st
   if (st != DT_OK) return st;
   int64_t len;
   int chunks;
-  st = plan_chunks(rows, vocab, cus, &len, &chunks);
+  st = plan_chunks(rows, vocab, cus, sample, &len, &chunks);
   if (st != DT_OK) return st;
   float2* part = nullptr;
   if (chunks > 1) {
@@ -288,21 +313,24 @@ int launch_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_st
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = aligned(logits, 16) && (row_stride % 4 == 0);
   dim3 grid((unsigned)chunks, (unsigned)rows);
+  const bool wide = !sample && rows >= cus;
+#define DT_LAUNCH_SCAN(V, S)                                                                                         \
+  do {                                                                                                              \
+    if (wide)                                                                                                       \
+      hipLaunchKernelGGL((argmax_chunks<V, S, kWideThreads, kWideUnroll>), grid, dim3(kWideThreads), 0, s, logits,  \
+                         vocab, row_stride, len, chunks, out_idx, part, g);                                         \
+    else                                                                                                            \
+      hipLaunchKernelGGL((argmax_chunks<V, S, kThreads, kUnroll>), grid, dim3(kThreads), 0, s, logits, vocab,       \
+                         row_stride, len, chunks, out_idx, part, g);                                                \
+  } while (0)
   if (sample) {
-    if (vec)
-      hipLaunchKernelGGL((argmax_chunks<true, true>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len, chunks,
-                         out_idx, part, g);
-    else
-      hipLaunchKernelGGL((argmax_chunks<false, true>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
-                         chunks, out_idx, part, g);
+    if (vec) DT_LAUNCH_SCAN(true, true);
+    else DT_LAUNCH_SCAN(false, true);
   } else {
-    if (vec)
-      hipLaunchKernelGGL((argmax_chunks<true, false>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
-                         chunks, out_idx, part, g);
-    else
-      hipLaunchKernelGGL((argmax_chunks<false, false>), grid, dim3(kThreads), 0, s, logits, vocab, row_stride, len,
-                         chunks, out_idx, part, g);
+    if (vec) DT_LAUNCH_SCAN(true, false);
+    else DT_LAUNCH_SCAN(false, false);
   }
+#undef DT_LAUNCH_SCAN
   if (chunks > 1)
     hipLaunchKernelGGL(argmax_merge, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, rows, vocab, chunks, part, out_idx);
   return launch_status();
@@ -329,7 +357,7 @@ extern "C" int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, 
 }
 
 extern "C" int dt_sample_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
-  return dt_argmax_rows_workspace_size(rows, vocab, bytes);
+  return dt::scan_workspace_size(rows, vocab, true, bytes);
 }
 
 extern "C" int dt_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, float temperature,

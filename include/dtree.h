@@ -225,7 +225,7 @@ int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
 
 /*
  * dt_sample_rows_workspace_size -- bytes of device workspace dt_sample_rows
- * needs (the same amount as dt_argmax_rows for the same shape).
+ * needs for `rows` rows of `vocab` entries on the current device.
  */
 int dt_sample_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes);
 
