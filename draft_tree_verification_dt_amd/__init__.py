@@ -118,6 +118,12 @@ class AttnLayout:
         return len(self.prefix_lens)
 
 
+def _row_stride(t, minimum):
+    """Row stride to pass for a tensor's first dimension: a single row may carry
+    any stride (numpy and torch give size-1 dimensions arbitrary ones)."""
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), minimum)
+
+
 def _stream(stream):
     import torch
 
@@ -149,14 +155,15 @@ def _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys):
     N, Hq, d = q.shape
     Hkv = k_tree.shape[1]
     for t, name in ((q, "q"), (k_tree, "k_tree")):
-        if t.stride(2) != 1 or t.stride(1) != d:
+        if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != d):
             raise ValueError(f"{name}: heads must be contiguous [rows][heads][d]")
     if k_prefix is not None and (k_prefix.stride(2) != 1):
         raise ValueError("k_prefix: head_dim must be contiguous")
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     p_rs = k_prefix.stride(0) if k_prefix is not None else 0
     p_hs = k_prefix.stride(1) if k_prefix is not None else 0
-    return _desc(layout, Hq, Hkv, d, scale, split_keys, q.stride(0), 0, k_tree.stride(0), p_rs, p_hs)
+    return _desc(layout, Hq, Hkv, d, scale, split_keys, _row_stride(q, Hq * d), 0, _row_stride(k_tree, Hkv * d),
+                 p_rs, p_hs)
 
 
 def dt_tree_attention_workspace_size(q, k_tree, k_prefix, layout, scale=None, split_keys=0):
@@ -185,7 +192,7 @@ def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, sca
     desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    desc.out_row_stride = out.stride(0)
+    desc.out_row_stride = _row_stride(out, q.shape[1] * q.shape[2])
     lib = _lib.load()
     need = ctypes.c_size_t(0)
     _check(lib.dt_tree_attention_workspace_size(ctypes.byref(desc), ctypes.byref(need)),
@@ -224,8 +231,8 @@ def dt_argmax_rows(logits, out=None, workspace=None, stream=None):
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.load().dt_argmax_rows(logits.data_ptr(), rows, vocab, logits.stride(0), out.data_ptr(), ws_ptr, ws_len,
-                                    _stream(stream))
+    st = _lib.load().dt_argmax_rows(logits.data_ptr(), rows, vocab, _row_stride(logits, vocab), out.data_ptr(), ws_ptr,
+                                    ws_len, _stream(stream))
     _check(st, "dt_argmax_rows")
     return out
 
@@ -253,7 +260,7 @@ def dt_sample_rows(logits, temperature, seed, offset, out=None, workspace=None, 
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.load().dt_sample_rows(logits.data_ptr(), rows, vocab, logits.stride(0), float(temperature),
+    st = _lib.load().dt_sample_rows(logits.data_ptr(), rows, vocab, _row_stride(logits, vocab), float(temperature),
                                     int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFFFFFFFFFF, out.data_ptr(),
                                     ws_ptr, ws_len, _stream(stream))
     _check(st, "dt_sample_rows")
@@ -300,7 +307,7 @@ class CommitArgs:
         kt0, kc0 = k_tree[0], k_cache[0]
         _, Hkv, d = kt0.shape
         for t in list(k_tree) + list(v_tree):
-            if t.stride() != kt0.stride() or t.stride(2) != 1 or t.stride(1) != d:
+            if t.stride() != kt0.stride() or t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != d):
                 raise ValueError("tree K/V: [rows][heads][d] with contiguous heads, all layers alike")
         for t in list(k_cache) + list(v_cache):
             if t.stride() != kc0.stride() or t.stride(2) != 1:
@@ -319,7 +326,7 @@ class CommitArgs:
         desc.prefix_lens = _ptr(layout.prefix_lens, ctypes.c_int32)
         desc.prefix_row_start = _ptr(layout.prefix_row_start, ctypes.c_int64)
         desc.cache_rows = _ptr(self.cache_rows, ctypes.c_int64)
-        desc.tree_row_stride = kt0.stride(0)
+        desc.tree_row_stride = _row_stride(kt0, Hkv * d)
         desc.cache_row_stride = kc0.stride(0)
         desc.cache_head_stride = kc0.stride(1)
         self.desc = desc
@@ -366,7 +373,7 @@ def dt_topk_rows(logits, k, out_token=None, out_logprob=None, workspace=None, st
             raise ValueError("outputs must be contiguous [rows, k]")
     if workspace is None:
         workspace = torch.empty(max(dt_topk_rows_workspace_size(rows, vocab, k), 256), dtype=torch.uint8, device=dev)
-    st = _lib.load().dt_topk_rows(logits.data_ptr(), rows, vocab, logits.stride(0), int(k), out_token.data_ptr(),
+    st = _lib.load().dt_topk_rows(logits.data_ptr(), rows, vocab, _row_stride(logits, vocab), int(k), out_token.data_ptr(),
                                   out_logprob.data_ptr(), workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "dt_topk_rows")
@@ -382,22 +389,23 @@ def dt_expand_depth(parent_score, child_logq, cand_token, w, beta, out=None, str
     import torch
 
     S, w_prev, k = child_logq.shape
-    if child_logq.stride(2) != 1 or child_logq.stride(1) != k:
+    if child_logq.stride(2) != 1 or (w_prev > 1 and child_logq.stride(1) != k):
         raise ValueError("child_logq: each sequence's [w_prev, k] block must be contiguous")
     for t in (parent_score, cand_token):
-        if t.stride(1) != 1:
+        if t.shape[1] > 1 and t.stride(1) != 1:
             raise ValueError("parent_score / cand_token rows must be contiguous")
     dev = child_logq.device
     if out is None:
         out = (torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.int32, device=dev),
                torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.float32, device=dev))
-    rs = out[0].stride(0)
-    if any(t.stride(0) != rs or t.stride(1) != 1 for t in out):
+    rs = _row_stride(out[0], w)
+    if any(_row_stride(t, w) != rs or (w > 1 and t.stride(1) != 1) for t in out):
         raise ValueError("outputs must share one row stride with contiguous rows")
-    st = _lib.load().dt_expand_depth(S, w_prev, k, int(w), float(beta), parent_score.data_ptr(), parent_score.stride(0),
-                                     child_logq.data_ptr(), child_logq.stride(0), cand_token.data_ptr(),
-                                     cand_token.stride(0), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
-                                     out[3].data_ptr(), rs, _stream(stream))
+    st = _lib.load().dt_expand_depth(S, w_prev, k, int(w), float(beta), parent_score.data_ptr(),
+                                     _row_stride(parent_score, w_prev), child_logq.data_ptr(),
+                                     _row_stride(child_logq, w_prev * k), cand_token.data_ptr(),
+                                     _row_stride(cand_token, k), out[0].data_ptr(), out[1].data_ptr(),
+                                     out[2].data_ptr(), out[3].data_ptr(), rs, _stream(stream))
     _check(st, "dt_expand_depth")
     return out
 

@@ -337,3 +337,72 @@ def test_construction_replays_from_a_hip_graph():
         for a, b in zip(eager, replayed):
             assert torch.equal(a, b), f"replay {rep}"
         assert int(replayed[4][0]) == B + 1
+
+
+def test_dartree_tree_verifies_end_to_end():
+    """A whole round on DARTree's tree: GPU construction (B = 64), tree attention
+    over a 2048-token prefix, greedy predictions planted on the tree, the walk
+    and the KV commit; attention, path and committed rows checked against the
+    oracle on the constructed tree."""
+    import torch
+
+    from _helpers import assert_attention_close, dev_bf16, host_f64
+    from gen import tensors as gten
+    from oracle import argmax as oarg, attention as oatt, commit as ocommit, walk as owalk
+
+    require_gpu()
+    r = grng.stream(21, "dartree-round")
+    gamma, V, K, W, B, beta = 16, 151936, 64, 12, 64, -0.2
+    Hq, Hkv, d, P = 32, 8, 128, 2048
+    base = _t((r.standard_normal((gamma, V)) * 3).astype(np.float32))
+    ctok, clp = dt.dt_topk_rows(base, K)
+    torch.cuda.synchronize()
+    clp_h, ctok_h = clp.cpu().numpy(), ctok.cpu().numpy()
+    sup = [torch.full((1, gamma, W), -1, dtype=t, device="cuda") for t in (torch.int32, torch.int32, torch.int32)]
+    sup.append(torch.full((1, gamma, W), float("-inf"), dtype=torch.float32, device="cuda"))
+    prev = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+    paths = [()]
+    for dd in range(gamma):
+        lq = _synthetic_head(clp_h[dd], paths, ctok_h[dd])[None]
+        dt.dt_expand_depth(prev, _t(lq), ctok[dd:dd + 1], W, beta, out=tuple(x[:, dd] for x in sup))
+        torch.cuda.synchronize()
+        par_h, cand_h = sup[0][0, dd].cpu().numpy(), sup[1][0, dd].cpu().numpy()
+        m = int((par_h >= 0).sum())
+        paths = [paths[p] + (int(c),) for p, c in zip(par_h[:m], cand_h[:m])]
+        prev = sup[3][:, dd]
+    root = 4242
+    print("dartree round: supertree built", flush=True)
+    tp, tt, td, ts, tn = dt.dt_prune_topb(sup[0], sup[2], sup[3], dev_i32([root]), B)
+    torch.cuda.synchronize()
+    n = int(tn.cpu()[0])
+    assert n == B + 1
+    parent = tp.cpu().numpy()[0, :n]
+    token = tt.cpu().numpy()[0, :n]
+    otree.check(parent)
+    # verification over the constructed tree
+    ops = gten.attention_operands(r, n, P, Hq, Hkv, d)
+    cache_k = np.zeros((P + n, Hkv, d), np.float32)
+    cache_v = np.zeros((P + n, Hkv, d), np.float32)
+    cache_k[:P], cache_v[:P] = ops["k_prefix"], ops["v_prefix"]
+    kc, vc, kt, vt = dev_bf16(cache_k), dev_bf16(cache_v), dev_bf16(ops["k_tree"]), dev_bf16(ops["v_tree"])
+    layout = dt.AttnLayout([0, n], [P], [0])
+    par_d = dev_i32(parent)
+    out = dt.dt_tree_attention(dev_bf16(ops["q"]), kt, vt, kc, vc, par_d, layout)
+    logits = gten.logits(r, n, 4096)
+    tok_small = (token % 4096).astype(np.int32)  # a 4096-token stand-in vocabulary for the target logits
+    tok_small[0] = root % 4096
+    gten.plant(r, logits, parent, tok_small, p=0.9, pick="first")
+    am = dt.dt_argmax_rows(_t(logits))
+    path, acc, bonus = dt.dt_accept_path([0, n], par_d, dev_i32(tok_small), am)
+    dt.dt_commit_kv(dt.CommitArgs(layout, [P + n], [kt], [vt], [kc], [vc]), path, acc)
+    torch.cuda.synchronize()
+    ref = oatt.tree_attention(ops["q"], ops["k_tree"], ops["v_tree"], ops["k_prefix"], ops["v_prefix"], parent)
+    assert_attention_close(host_f64(out), ref, what="dartree tree")
+    wpath, wL, wb = owalk.accept_path(parent, tok_small, oarg.argmax_rows(logits))
+    assert int(acc.cpu()[0]) == wL and int(bonus.cpu()[0]) == wb
+    assert list(path.cpu().numpy()[:wL + 1]) == wpath
+    full = np.full(n, -1)
+    full[:wL + 1] = wpath
+    wk, wv = ocommit.commit_kv(cache_k, cache_v, ops["k_tree"], ops["v_tree"], full, [wL], [0, n], [P], [0])
+    assert np.array_equal(kc.float().cpu().numpy(), wk) and np.array_equal(vc.float().cpu().numpy(), wv)
+    assert wL >= 2
