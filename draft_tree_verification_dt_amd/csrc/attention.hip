@@ -480,11 +480,15 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
           if (!((vh >> kk) & 1ull)) sc[bb][j] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // row max as a tree (independent operations at every level, no serial chain)
+    float t[16];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+    for (int i = 0; i < 16; ++i) t[i] = fmaxf(sc[i >> 3][(i & 7) * 2], sc[i >> 3][(i & 7) * 2 + 1]);
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sc[bb][j], sc[bb][j + 1]));
+    for (int i = 0; i < 8; ++i) t[i] = fmaxf(t[i], t[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = fmaxf(t[i], t[i + 4]);
+    float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     mx = max_halves(mx);
     const float mt = mx * c;
     // Rescale only when a row's max jumps by more than the slack (rare after
@@ -503,6 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     }
     const float neg_m = -m_run;
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -512,8 +517,10 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
         pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][j + 1], c, neg_m));
         pb[bb][j >> 3][j & 7] = pr[0];
         pb[bb][j >> 3][(j & 7) + 1] = pr[1];
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);  // sums the rounded probabilities
+        const int q = (j >> 1) & 3;
+        ls[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[q], false);  // sums the rounded probabilities
       }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
   // The whole step for one wave (the schedule without ping-pong).
   auto compute = [&](int step, Stage stage) __attribute__((always_inline)) {
