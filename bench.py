@@ -519,7 +519,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification path of one round is "
-              "single-GPU here, see DESIGN.md for how it would shard.", file=sys.stderr)
+              "single-GPU; sharding by sequence, KV head, vocabulary or prefix is a design note, not code.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -105,8 +105,8 @@ def load():
 
         if not os.path.exists(LIB_PATH):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m draft_tree_verification_dt_amd.build` "
-                "(or __graft_entry__.build()); there is no fallback implementation")
+                f"{LIB_PATH} is missing: build it with `python -m draft_tree_verification_dt_amd.build`"
+                "; there is no fallback implementation")
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

@@ -28,7 +28,7 @@ extern "C" const char* dt_status_string(int status) {
     case DT_ERR_SHAPE: return "a count, size, stride or offset is out of range or misaligned";
     case DT_ERR_TREE: return "parent array is not a topologically numbered tree (parent[0] = -1, 0 <= parent[i] < i)";
     case DT_ERR_VALUE: return "candidate table violates its contract (finite, <= 0, rows non-increasing, distinct tokens)";
-    case DT_ERR_UNSUPPORTED: return "request not supported by this build";
+    case DT_ERR_UNSUPPORTED: return "request not supported by this library";
     case DT_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
     case DT_ERR_HIP: return "a HIP runtime call failed";
     case DT_ERR_NOMEM: return "temporary host memory could not be obtained";

@@ -66,7 +66,7 @@ enum dt_status {
   DT_ERR_SHAPE = -2,       /* a count, size, stride or offset is out of range or misaligned */
   DT_ERR_TREE = -3,        /* a (host) parent array is not a topologically numbered tree */
   DT_ERR_VALUE = -4,       /* candidate table: unsorted row, non-finite or positive log-prob, repeated token */
-  DT_ERR_UNSUPPORTED = -5, /* a valid request this build does not implement (e.g. head_dim not 64/128) */
+  DT_ERR_UNSUPPORTED = -5, /* a valid request the library does not implement (e.g. head_dim not 64/128) */
   DT_ERR_WORKSPACE = -6,   /* workspace NULL, too small or not 256-byte aligned */
   DT_ERR_HIP = -7,         /* a HIP runtime call failed */
   DT_ERR_NOMEM = -8        /* temporary host memory could not be obtained (dt_build_tree) */

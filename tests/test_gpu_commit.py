@@ -143,7 +143,7 @@ def test_commit_full_round_36_layers():
 
 
 def test_two_rounds_attend_over_the_committed_cache():
-    """Round 1: attention, argmax, walk, commit. Round 2: a new tree attends over
+    """First verification round: attention, argmax, walk, commit. Second: a new tree attends over
     the P + L + 1 committed rows; its output matches the oracle evaluated on the
     oracle-committed cache."""
     import torch
@@ -179,5 +179,5 @@ def test_two_rounds_attend_over_the_committed_cache():
                                 dev_i32(p2), dt.AttnLayout([0, n2], [P2], [0]))
     torch.cuda.synchronize()
     ref = oatt.tree_attention(ops2["q"], ops2["k_tree"], ops2["v_tree"], wk[:P2], wv[:P2], p2)
-    assert_attention_close(host_f64(out2), ref, what="round 2")
+    assert_attention_close(host_f64(out2), ref, what="second verification round")
     assert L1 > 0
