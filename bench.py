@@ -160,6 +160,11 @@ class Round:
         """One round. `events` (start, end), if given, bracket the round's
         attention calls on the stream they run on."""
         t = self.build_and_upload()
+        self.device_part(t, events)
+        self.advance()
+
+    def device_part(self, t, events=None):
+        """The round's GPU calls for candidate table t (the tree already on the device)."""
         if events is not None:
             events[0].record()
         for l in range(self.w.layers):
@@ -181,6 +186,8 @@ class Round:
             raise self.dt.DtError(st, "dt_accept_path")
         if self.do_commit:
             self.commit()
+
+    def advance(self):
         self.step_idx += 1
 
     def sample(self, lg, offset, temperature=None):
@@ -250,6 +257,32 @@ def tree_shape(rnd):
                 hist[int(dd)] = hist.get(int(dd), 0) + int(c)
     return {"depth_hist": [hist.get(i, 0) for i in range(max(hist) + 1)], "max_depth": max(hist),
             "tables": len(rnd.trees)}
+
+
+def time_round_graph(rnd, reps=5):
+    """The round's GPU calls (36 attention calls, the row scan, the walk, and the
+    commit when the step has it) captured in one HIP graph and replayed: the
+    device-side time of a round without host launch overhead."""
+    torch = rnd.torch
+    rnd.device_part(0)
+    torch.cuda.synchronize()
+    import ctypes
+
+    graph = torch.cuda.CUDAGraph()
+    saved = rnd.stream
+    with torch.cuda.graph(graph):
+        rnd.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the capturing stream
+        rnd.device_part(0)
+    rnd.stream = saved
+    graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
 def time_on_stream(rnd, fn, reps):
@@ -565,6 +598,7 @@ def main():
     smp_ms = time_sample_calls(rnd, reps=10)
     com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
     db, draft = time_draft_build(rnd)
+    graph_ms = time_round_graph(rnd)
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
@@ -577,6 +611,7 @@ def main():
                    "tree_nodes": w.nodes[0] if len(set(w.nodes)) == 1 else w.nodes, "layers": w.layers,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "vocab": w.vocab, "tree": w.tree},
         "us_per_round": round(ms_per_step * 1e3, 1),
+        "us_per_round_device_graph": round(graph_ms * 1e3, 1),
         "roofline": {"bound": "mfma", "kernel": "dt_tree_attention call (tree_attn_fwd + tree_attn_combine)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
