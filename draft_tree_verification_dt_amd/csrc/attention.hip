@@ -729,13 +729,19 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 // Merge the per-chunk partials of split sequences. A thread owns eight
 // consecutive dims of one (node, query head) row (one 16-byte load per chunk),
 // so the threads of a row read each chunk's partial as one contiguous line.
-template <int D>
+// One partial row per (row, eight-dim slice) thread, or, with G > 1, G threads
+// per (row, slice) that take every G-th chunk and merge their running (m, l, O)
+// through cross-lane shuffles at the end (for many chunks and few rows, so that
+// more threads carry the loads). The G * D/8 threads of a row are adjacent lanes
+// of one wave.
+template <int D, int G>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
-  constexpr int kTpr = D / 8;          // threads per row
-  constexpr int kRpb = 256 / kTpr;     // rows per block
-  const int row = blockIdx.x * kRpb + threadIdx.x / kTpr;
+  constexpr int kTpr = D / 8;          // threads per row and chunk group
+  constexpr int kRpb = 256 / (kTpr * G);  // rows per block
+  const int row = blockIdx.x * kRpb + threadIdx.x / (kTpr * G);
+  const int gi = (threadIdx.x / kTpr) % G;
   const int c8 = threadIdx.x % kTpr;
-  if (row >= p.comb_rows) return;
+  if (row >= p.comb_rows) return;  // the row's G * kTpr lanes leave together
   int s = -1;
   for (int i = 0; i < p.nseq; ++i)
     if (p.seq[i].splits > 1 && p.seq[i].comb_start <= row) s = i;
@@ -748,17 +754,17 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   const int64_t prow0 = (int64_t)sg.part_base + r;
   const int64_t kstride = (int64_t)sg.n * p.Hq;
   const uint4* po = reinterpret_cast<const uint4*>(p.part_o);  // eight fp16 values per thread
-  // Chunks are merged eight at a time (their loads in flight together): the
-  // batch's maximum first, then every chunk with one weight.
+  // Chunks gi, gi + G, ... are merged eight at a time (their loads in flight
+  // together): the batch's maximum first, then every chunk with one weight.
   constexpr int kBatch = 8;
   float m = -INFINITY, l = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < sg.splits; k0 += kBatch) {
+  for (int k0 = gi; k0 < sg.splits; k0 += G * kBatch) {
     float4 ml[kBatch];
     uint4 v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int k = min(k0 + u, sg.splits - 1);
+      const int k = min(k0 + u * G, sg.splits - 1);
       const int64_t prow = prow0 + k * kstride;
       ml[u] = p.part_ml[prow];
       v[u] = po[prow * kTpr + c8];
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      ok[u] = k0 + u < sg.splits && ml[u].y > 0.f;
+      ok[u] = k0 + u * G < sg.splits && ml[u].y > 0.f;
       if (ok[u]) mb = fmaxf(mb, ml[u].x);
     }
     if (mb == -INFINITY) continue;  // nothing visible yet
@@ -788,6 +794,23 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
       for (int e = 0; e < 8; ++e) o[e] += ws * (float)h[e];
     }
   }
+  if constexpr (G > 1) {
+#pragma unroll
+    for (int off = kTpr; off < kTpr * G; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], off);
+      const float mn = fmaxf(m, m2);
+      if (mn == -INFINITY) continue;  // neither side has seen a visible key
+      const float a1 = __builtin_amdgcn_exp2f(m - mn), a2 = __builtin_amdgcn_exp2f(m2 - mn);
+      l = l * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+      m = mn;
+    }
+    if (gi != 0) return;
+  }
   const float inv = 1.f / l;
   __bf16 o8[8];
 #pragma unroll
@@ -803,6 +826,7 @@ struct Plan {
   std::vector<AttnParams> launches;  // one per group of <= kMaxSeqs sequences
   std::vector<int> grid;             // workgroups per launch
   std::vector<int> comb_grid;        // combine blocks per launch (0 = none)
+  std::vector<int> comb_groups;      // chunk groups per combine row (1 or 4)
   std::vector<size_t> lds;           // dynamic LDS bytes per launch
   size_t ws_bytes = 0;
 };
@@ -967,7 +991,12 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
     a.comb_rows = comb;
     plan->launches.push_back(a);
     plan->grid.push_back(a.per_xcd * kXcds);
-    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8)) : 0);
+    // many chunks per row: four threads share each (row, slice), more threads carry the loads
+    int max_splits = 1;
+    for (int i = 0; i < a.nseq; ++i) max_splits = std::max(max_splits, a.seq[i].splits);
+    const int cg = max_splits > 8 ? 4 : 1;
+    plan->comb_groups.push_back(cg);
+    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8 * cg)) : 0);
     plan->lds.push_back(dynamic_lds(launch_max_n, g, wm));
   }
   plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(_Float16), 256) +
@@ -1054,10 +1083,20 @@ extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const 
     if (a.total_items == 0) continue;
     if (D == 128) {
       launch_fwd<128>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
-      if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<128>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      if (plan.comb_grid[li]) {
+        if (plan.comb_groups[li] > 1)
+          hipLaunchKernelGGL((tree_attn_combine<128, 4>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+        else
+          hipLaunchKernelGGL((tree_attn_combine<128, 1>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      }
     } else {
       launch_fwd<64>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
-      if (plan.comb_grid[li]) hipLaunchKernelGGL(tree_attn_combine<64>, dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      if (plan.comb_grid[li]) {
+        if (plan.comb_groups[li] > 1)
+          hipLaunchKernelGGL((tree_attn_combine<64, 4>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+        else
+          hipLaunchKernelGGL((tree_attn_combine<64, 1>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      }
     }
     st = launch_status();
     if (st != DT_OK) return st;
