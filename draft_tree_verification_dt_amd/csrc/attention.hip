@@ -882,9 +882,16 @@ size_t dynamic_lds(int max_n, int g, int wm) {
 // eight waves split the keys of each step instead.
 int choose_wm(const dt_attn_desc* d, int g) {
   int max_rows = 0;
-  for (int s = 0; s < d->num_seqs; ++s)
-    max_rows = std::max(max_rows, (d->node_offsets[s + 1] - d->node_offsets[s]) * g);
-  if (max_rows <= 64) return 2;
+  int64_t max_keys = 0;
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int n = d->node_offsets[s + 1] - d->node_offsets[s];
+    max_rows = std::max(max_rows, n * g);
+    max_keys = std::max<int64_t>(max_keys, (int64_t)d->prefix_lens[s] + n);
+  }
+  // At most 64 rows over a long prefix the call streams K/V from HBM: 128-row
+  // tiles (half the row groups idle) keep two 64 KB stages in flight where the
+  // 64 x 256 shape has room for one 128 KB stage only.
+  if (max_rows <= 64) return max_keys > 16 * kBN ? 4 : 2;
   if (max_rows <= 128) return 4;
   return 8;
 }
