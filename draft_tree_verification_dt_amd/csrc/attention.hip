@@ -13,7 +13,8 @@
 //  * A workgroup of eight waves (two per SIMD, one workgroup per CU); each
 //    wave owns 32 query rows. The workgroup is WM row groups x WN key slices
 //    (WM * WN = 8): 256 rows x 64 keys per step for large trees, 128 x 128 or
-//    64 x 256 for small ones. Every K/V tile staged in LDS serves all the
+//    64 x 256 for small ones (tiny trees over a long prefix take 128 x 128 even
+//    with half its rows empty, for a deeper K/V ring). Every K/V tile staged in LDS serves all the
 //    workgroup's rows, and the key slices of one row group are merged through
 //    LDS at the end.
 //  * Scores are computed transposed, S^T = K Q^T, so every lane holds the
