@@ -645,6 +645,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 
   // ---- epilogue: lane (lr, hh) holds O^T[d][row lr] for d = 32i + 8(j/4) + 4hh + (j%4) ----
   float l_tot = sum_halves(l_run);
+  const int wrow0 = row0 + wm * kWaveRows;  // the wave's first query row
 
   if constexpr (WN > 1) {
     // merge the key slices of each row group through LDS (stage 0 is free now)
@@ -684,46 +685,96 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
           for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] * a1 + src[(i * 16 + j) * 64 + lane] * a2;
       }
     }
-  }
-  if (wn != 0 || !row_ok) return;
-
-  if (sg.splits == 1) {
-    const float inv = 1.f / l_tot;
-    bf16_bits* orow = p.out + (int64_t)(sg.node_off + my_node) * p.out_rs + (int64_t)my_qh * D;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        __bf16 o4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[i][j4 * 4 + e] * inv);
-        *reinterpret_cast<uint2*>(orow + i * 32 + j4 * 8 + hh * 4) = *reinterpret_cast<uint2*>(o4);
-      }
+    if (wn != 0 || !row_ok) return;
   } else {
-    // Partial for the merge: the row's unnormalised output scaled by a power
-    // of two 2^-e so that every |value| < 1, stored as fp16 (an exact scaling,
-    // so the stored values keep 11 significant bits relative to the row's
-    // largest entry whatever the magnitude of V), with (m, l, 2^e).
-    float amax = 0.f;
+    if (wrow0 >= nrows) return;
+  }
+
+  // An unsplit row is final: O / l in bf16. A split row is a partial for the
+  // merge: the unnormalised output scaled by a power of two 2^-e so that every
+  // |value| < 1, in fp16 (an exact scaling, so the stored values keep 11
+  // significant bits relative to the row's largest entry whatever the
+  // magnitude of V), with (m, l, 2^e) beside it.
+  const bool part = sg.splits > 1;
+  float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+  for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(acc[i][j]));
-    amax = max_halves(amax);
-    const int e = min(((int)((__float_as_uint(amax) >> 23) & 255)) - 126, 127);  // amax < 2^e (or e = 127)
-    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(acc[i][j]));
+  amax = max_halves(amax);
+  const int e = min(((int)((__float_as_uint(amax) >> 23) & 255)) - 126, 127);  // amax < 2^e (or e = 127)
+  const float mul = part ? __builtin_amdgcn_ldexpf(1.f, -e) : 1.f / l_tot;
+  // the four-value groups (d = 32i + 8j4 + 4hh ..) of this lane's row, in the output's 16-bit format
+  auto pack = [&](int i, int j4) __attribute__((always_inline)) -> uint2 {
+    if (part) {
+      _Float16 h4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h4[q] = (_Float16)(acc[i][j4 * 4 + q] * mul);
+      return *reinterpret_cast<uint2*>(h4);
+    }
+    __bf16 b4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b4[q] = (__bf16)(acc[i][j4 * 4 + q] * mul);
+    return *reinterpret_cast<uint2*>(b4);
+  };
+  // first element of a row's output (bf16 O, or the fp16 partial of this split)
+  auto row_dst = [&](int node, int qh) __attribute__((always_inline)) -> uint16_t* {
+    return part ? reinterpret_cast<uint16_t*>(p.part_o) +
+                      ((int64_t)sg.part_base + ((int64_t)split * sg.n + node) * p.Hq + qh) * D
+                : p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D;
+  };
+  if (part && row_ok && hh == 0) {
     const int64_t prow = (int64_t)sg.part_base + ((int64_t)split * sg.n + my_node) * p.Hq + my_qh;
-    _Float16* po = p.part_o + prow * D;
+    p.part_ml[prow] = make_float4(m_run, l_tot, __builtin_amdgcn_ldexpf(1.f, e), 0.f);
+  }
+
+  if constexpr (WN > 1) {
+    // few rows per workgroup: every lane stores its own row's groups
+    uint16_t* orow = row_dst(my_node, my_qh);
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        _Float16 h4[4];
+      for (int j4 = 0; j4 < 4; ++j4) *reinterpret_cast<uint2*>(orow + i * 32 + j4 * 8 + hh * 4) = pack(i, j4);
+  } else {
+    // 256 rows per workgroup, all of them finishing together across the chip:
+    // the wave's 32 rows leave through a wave-private LDS buffer (32 rows of
+    // 2D bytes, 16-byte chunks XOR-swizzled by row) so that every store
+    // instruction writes whole rows -- D/8 adjacent lanes store one row's
+    // chunks, 512/D rows per instruction, and the rows of one node's query
+    // heads are adjacent in memory -- instead of 16-byte pieces of 32 rows.
+    // The buffer is a stage that no wave reads any more: not the last one
+    // (the other group may still be reading it); the group of waves 0-3
+    // takes the stage after it, the other group the stage after that, each
+    // wave a quarter of that stage.
+    static_assert(NST == 4, "one key slice only in the ping-pong schedule");
+    const int st = (max(nsteps - 1, 0) + 1 + (wave >> 2)) & 3;
+    const int wq = wave & 3;
+    char* ob = ((wq < 2) ? (st == 0 ? k0 : st == 1 ? k1 : st == 2 ? k2 : k3)
+                         : (st == 0 ? v0 : st == 1 ? v1 : st == 2 ? v2 : v3)) +
+               (wq & 1) * (kWaveRows * D * 2);
+    constexpr int kCh = D / 8;               // 16-byte chunks per row
+    constexpr int kRowsPerStore = 64 / kCh;  // rows one store instruction covers
+    auto swz = [](int r) __attribute__((always_inline)) { return (D == 128 ? r : (r >> 1)) & (kCh - 1); };
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h4[q] = (_Float16)(acc[i][j4 * 4 + q] * down);
-        *reinterpret_cast<uint2*>(po + i * 32 + j4 * 8 + hh * 4) = *reinterpret_cast<uint2*>(h4);
-      }
-    if (hh == 0) p.part_ml[prow] = make_float4(m_run, l_tot, __builtin_amdgcn_ldexpf(1.f, e), 0.f);
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        *reinterpret_cast<uint2*>(ob + lr * (2 * D) + (((i * 4 + j4) ^ swz(lr)) << 4) + hh * 8) = pack(i, j4);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's buffer writes are complete
+    const int sr = lane / kCh, sc16 = lane % kCh;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kStores = kWaveRows / kRowsPerStore;
+    u32x4 v[kStores];  // all reads in flight together, then the stores
+#pragma unroll
+    for (int k = 0; k < kStores; ++k) {
+      const int r = k * kRowsPerStore + sr;
+      v[k] = *reinterpret_cast<const u32x4*>(ob + r * (2 * D) + ((sc16 ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int k = 0; k < kStores; ++k) {
+      const int row = wrow0 + k * kRowsPerStore + sr;
+      if (row < nrows) *reinterpret_cast<u32x4*>(row_dst(row / g, head * g + row % g) + sc16 * 8) = v[k];
+    }
   }
 }
 
