@@ -277,37 +277,6 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   uint32_t* masks = dyn + p.max_n;
   float* merge_ml = reinterpret_cast<float*>(masks + p.mask_rows * p.mask_words);
 
-  // ---- Q rows (B operand of S^T = K Q^T): lane holds row lr, dims 16k + 8hh .. +7 ----
-  bf16x8 qreg[KS];
-  {
-    const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + k * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
-      qreg[k] = *reinterpret_cast<bf16x8*>(&v);
-    }
-  }
-
-  // ---- ancestor bitmasks of this tile's nodes (only if tree keys are visited) ----
-  if (key_hi > sg.P) {
-    for (int i = tid; i <= node_hi; i += kThreads) par_s[i] = (uint32_t)p.parent[sg.node_off + i];
-    const int nmask = (node_hi - node_lo + 1) * p.mask_words;
-    for (int i = tid; i < nmask; i += kThreads) masks[i] = 0u;
-    __syncthreads();
-    for (int t = tid; t <= node_hi - node_lo; t += kThreads) {
-      uint32_t* row = masks + t * p.mask_words;
-      int j = node_lo + t;
-      // Walk to the root; parent[j] < j bounds the walk even for a malformed array.
-      for (;;) {
-        row[j >> 5] |= 1u << (j & 31);
-        const int pj = (int)par_s[j];
-        if (pj < 0 || pj >= j) break;
-        j = pj;
-      }
-    }
-    __syncthreads();
-  }
-
   // ---- K/V stage loads ----
   const char* kp_base = reinterpret_cast<const char*>(p.kp);
   const char* vp_base = reinterpret_cast<const char*>(p.vp);
@@ -359,6 +328,49 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       }
     }
   };
+
+  // The first stage is requested before anything else (Q, the masks), so
+  // that its latency overlaps the rest of the set-up; the tree's parents go
+  // first when this item needs them, so that waiting for them does not wait
+  // for the stage.
+  const bool need_mask = key_hi > sg.P;
+  uint32_t par0 = 0;
+  if (need_mask && tid <= node_hi) par0 = (uint32_t)p.parent[sg.node_off + tid];
+  if (nsteps > 0) issue(key_lo, Stage{k0, v0});
+
+  // ---- Q rows (B operand of S^T = K Q^T): lane holds row lr, dims 16k + 8hh .. +7 ----
+  bf16x8 qreg[KS];
+  {
+    const bf16_bits* qrow = p.q + (int64_t)(sg.node_off + my_node) * p.q_rs + (int64_t)my_qh * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + k * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+      qreg[k] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  // ---- ancestor bitmasks of this tile's nodes (only if tree keys are visited) ----
+  // Its barriers wait for LDS traffic only (the first stage's loads stay in
+  // flight), and the first pass of parents was read before that stage.
+  if (need_mask) {
+    if (tid <= node_hi) par_s[tid] = par0;
+    for (int i = tid + kThreads; i <= node_hi; i += kThreads) par_s[i] = (uint32_t)p.parent[sg.node_off + i];
+    const int nmask = (node_hi - node_lo + 1) * p.mask_words;
+    for (int i = tid; i < nmask; i += kThreads) masks[i] = 0u;
+    stage_barrier();
+    for (int t = tid; t <= node_hi - node_lo; t += kThreads) {
+      uint32_t* row = masks + t * p.mask_words;
+      int j = node_lo + t;
+      // Walk to the root; parent[j] < j bounds the walk even for a malformed array.
+      for (;;) {
+        row[j >> 5] |= 1u << (j & 31);
+        const int pj = (int)par_s[j];
+        if (pj < 0 || pj >= j) break;
+        j = pj;
+      }
+    }
+    stage_barrier();
+  }
 
   // ---- running state ----
   f32x16 acc[DB];
@@ -600,7 +612,6 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       stage_barrier();
       x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
     };
-    if (nsteps > 0) issue(key_lo, Stage{k0, v0});
     if (nsteps > 1) issue(key_lo + KN, Stage{k1, v1});
     if (!grp_b) {
       for (int s0 = 0; s0 < nsteps; s0 += 4) {
@@ -629,8 +640,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       if (grp_b) pv_product(tail.v);
     }
   } else {
-  // prologue: the first NST - 1 stages (one if NST == 1)
-  if (nsteps > 0) issue(key_lo, Stage{k0, v0});
+  // prologue: the first NST - 1 stages (one if NST == 1); the first is in flight already
   if constexpr (NST > 2) {
     if (nsteps > 1) issue(key_lo + KN, Stage{k1, v1});
     if (nsteps > 2) issue(key_lo + 2 * KN, Stage{k2, v2});
