@@ -250,8 +250,12 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
-  const int wm = wave % WM;  // row group
-  const int wn = wave / WM;  // key slice
+  // Row group and key slice of this wave. Waves go round-robin over the four
+  // SIMDs, so with this order the two waves of a SIMD hold different row
+  // groups whenever WN > 1: a tile whose last row groups are empty (a small
+  // tree) leaves one working wave on every SIMD instead of two on half of them.
+  const int wm = wave / WN;  // row group
+  const int wn = wave % WN;  // key slice
   const int lr = lane & 31;  // query row within a 32-row block
   const int hh = lane >> 5;  // half-wave
   const int g = p.g;
@@ -264,6 +268,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   const int my_qh = head * g + (row_ok ? my_row % g : 0);
   const int node_lo = row0 / g;
   const int node_hi = min(sg.n - 1, (min(row0 + RM, nrows) - 1) / g);
+  // a wave whose 32 rows are all past the tree's last row only loads and
+  // synchronises; it computes nothing
+  const bool wave_active = row0 + wm * kWaveRows < nrows;
 
   // ---- key range of this work item ----
   const int key_lo = split * p.chunk;
@@ -537,6 +544,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   };
   // The whole step for one wave (the schedule without ping-pong).
   auto compute = [&](int step, Stage stage) __attribute__((always_inline)) {
+    if (!wave_active) return;
     s_product(stage.k + wn * T::kBytes);
     softmax(step);
     pv_product(stage.v + wn * T::kBytes);
@@ -584,6 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     // tile s + 4 at phase 2s + 4, and each tile is loaded two steps ahead.
     const bool grp_b = wave >= 4;
     auto x_block = [&](int s, Stage cur, Stage prev) __attribute__((always_inline)) {
+      if (!wave_active) return;
       if (s > 0) pv_product(prev.v);
       s_product(cur.k);
     };
@@ -603,12 +612,12 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       even_barrier(s, U);
       x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
       stage_barrier();
-      softmax(s);
+      if (wave_active) softmax(s);
     };
     auto group_b = [&](int s, auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       even_barrier(s, U);
-      if (s > 0) softmax(s - 1);
+      if (s > 0 && wave_active) softmax(s - 1);
       stage_barrier();
       x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
     };
@@ -634,10 +643,10 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       const Stage tail = (last & 3) == 0 ? Stage{k0, v0} : (last & 3) == 1 ? Stage{k1, v1}
                        : (last & 3) == 2 ? Stage{k2, v2} : Stage{k3, v3};
       stage_barrier();
-      if (!grp_b) pv_product(tail.v);
-      else softmax(last);
+      if (wave_active && !grp_b) pv_product(tail.v);
+      else if (wave_active) softmax(last);
       stage_barrier();
-      if (grp_b) pv_product(tail.v);
+      if (wave_active && grp_b) pv_product(tail.v);
     }
   } else {
   // prologue: the first NST - 1 stages (one if NST == 1); the first is in flight already
