@@ -455,11 +455,13 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   auto s_product = [&](const char* kt) __attribute__((always_inline)) {
     bf16x8 ka[KS];
     load_k(kt, ka, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
       sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[0] : f32x16{}, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_k(kt, ka, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
       sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[1] : f32x16{}, 0, 0, 0);
