@@ -329,6 +329,44 @@ def time_commit_calls(rnd, reps):
     return ms, moved, acc
 
 
+def time_small_tree(rnd, reps=40, n=16):
+    """dt_tree_attention for an n-node chain (parent[i] = i - 1) over the first
+    sequence's own prefix, one call per layer cache in turn (so the caches rotate
+    through 36 x 34 MB): the small-tree case, bound by streaming the prefix K/V
+    from HBM. Mean call time in ms from HIP events on the library's stream, the
+    call's algorithmic bytes and flops."""
+    import ctypes
+
+    torch, dt, w = rnd.torch, rnd.dt, rnd.w
+    from gen import tensors as gten
+
+    P, Hq, Hkv, d = w.prefix_lens[0], w.Hq, w.Hkv, w.d
+    sc = 1.0 / np.sqrt(d)
+    q = gten.device_randn_bf16((n, Hq, d), w.seed, "chain-q", scale=sc)
+    kt = gten.device_randn_bf16((n, Hkv, d), w.seed, "chain-kt", scale=sc)
+    vt = gten.device_randn_bf16((n, Hkv, d), w.seed, "chain-vt", scale=sc)
+    par = torch.arange(-1, n - 1, dtype=torch.int32, device=rnd.dev)
+    out = torch.empty((n, Hq, d), dtype=torch.bfloat16, device=rnd.dev)
+    layout = dt.AttnLayout([0, n], [P], [int(rnd.starts[0])])
+    desc = dt._attn_geometry(q, kt, rnd.kp[0], layout, None, 0)
+    ws_n = dt.dt_tree_attention_workspace_size(q, kt, rnd.kp[0], layout)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=rnd.dev)
+    dref = ctypes.byref(desc)
+
+    def call(i):
+        l = i % w.layers
+        st = rnd.lib.dt_tree_attention(dref, q.data_ptr(), kt.data_ptr(), vt.data_ptr(), rnd.kp[l].data_ptr(),
+                                       rnd.vp[l].data_ptr(), par.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                                       ws.numel(), rnd.stream)
+        if st != 0:
+            raise dt.DtError(st, "dt_tree_attention")
+
+    ms = time_on_stream(rnd, call, reps)
+    nbytes = 2 * P * Hkv * d * 2 + n * (2 * Hq * d * 2 + 2 * Hkv * d * 2 + 4)
+    flops = 4.0 * d * Hq * (n * P + n * (n + 1) // 2)
+    return ms, nbytes, flops
+
+
 class DraftBuild:
     """DARTree's construction kernels at the pages' pruned configuration: gamma = 16
     draft positions over the vocabulary, K = 64 candidates, width W = 12, beta =
@@ -599,6 +637,15 @@ def main():
     com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
     db, draft = time_draft_build(rnd)
     graph_ms = time_round_graph(rnd)
+    small = None
+    if w.num_seqs == 1:
+        ch_ms, ch_bytes, ch_flops = time_small_tree(rnd)
+        ch_gbs = ch_bytes / (ch_ms / 1e3) / 1e9
+        small = {"workload": f"16-node chain (parent[i] = i - 1) over the same {w.prefix_lens[0]}-token prefix",
+                 "bound": "hbm", "us": round(ch_ms * 1e3, 2), "achieved": round(ch_gbs, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(ch_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": ch_bytes,
+                 "TFLOP/s": round(ch_flops / (ch_ms / 1e3) / 1e12, 1),
+                 "tree_over_chain_time": round(att_mean_ms / ch_ms, 2)}
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
@@ -627,6 +674,7 @@ def main():
                    "frac_hbm": argmax_bytes / (smp_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "commit": {"kernel": "dt_commit_kv, all layers in one call", "us": com_ms * 1e3, "bytes": com_bytes,
                    "GB/s": com_bytes / (com_ms / 1e3) / 1e9, "accept_len": com_acc.tolist()},
+        "small_tree": small,
         "draft_tree": dict(draft, kernels="dt_topk_rows, dt_expand_depth (x16 in the chain), dt_prune_topb"),
         "step_variant": {"temperature": args.temperature, "commit": bool(args.commit)},
         "parity": None,
