@@ -176,3 +176,39 @@ def test_round_planted_b128():
     gten.plant(grng.stream(w.seed, "plant"), lg, p, t, p=w.plant_p, pick="first")
     print("planted b128 round", flush=True)
     _check_walk([p], [t], lg, np.array([0, w.nodes[0]]))
+
+
+@pytest.mark.parametrize("name,shape", [("b256", "heap"), ("b256", "heap-narrow"), ("chain16", "chain"),
+                                        ("ragged", "heap-narrow"), ("long", "heap-narrow")])
+def test_round_planted_full_size(name, shape):
+    """A whole round's greedy verification at full size: every sequence's tree
+    (the literal best-first heap, its deep k = 2 variant, or the chain), target
+    logits over the 151936-token vocabulary drawn on the device with p = 0.8
+    planting on each node's first child, then arg-max and the walk, all
+    compared bit for bit with the oracle on the same logits."""
+    import torch
+
+    require_gpu()
+    w = gconf.get(name)
+    offs = w.node_offsets()
+    parents, tokens = [], []
+    for s, n in enumerate(w.nodes):
+        p, t = tree(shape, n, w.seed * 1000 + s)
+        parents.append(p)
+        tokens.append(t)
+    lg = gten.device_logits(w.total_nodes, w.vocab, w.seed, "walk-full", shape)
+    for s in range(w.num_seqs):
+        gten.device_plant(grng.stream(w.seed, "walk-plant", shape, s), lg, int(offs[s]), parents[s], tokens[s],
+                          p=w.plant_p)
+    print(f"planted full round {name} {shape}: {w.total_nodes} x {w.vocab}", flush=True)
+    am = dt.dt_argmax_rows(lg)
+    path, L, bonus = dt.dt_accept_path(offs, dev_i32(np.concatenate(parents)), dev_i32(np.concatenate(tokens)), am)
+    torch.cuda.synchronize()
+    am_ref = oarg.argmax_rows(lg.cpu().numpy())
+    np.testing.assert_array_equal(am.cpu().numpy(), am_ref)
+    path, L, bonus = path.cpu().numpy(), L.cpu().numpy(), bonus.cpu().numpy()
+    want = owalk.batch_accept_path(np.concatenate(parents), np.concatenate(tokens), am_ref, offs)
+    for s, (wpath, wL, wbonus) in enumerate(want):
+        a = offs[s]
+        assert L[s] == wL and bonus[s] == wbonus, (s, L[s], wL, bonus[s], wbonus)
+        assert list(path[a:a + wL + 1]) == wpath
