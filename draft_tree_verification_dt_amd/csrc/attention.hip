@@ -411,37 +411,44 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     }
   };
   // V^T operands of d-blocks i0 .. i0+1, (i, bb, sub): d = 32i .., keys 32bb + 16sub ..
-  // The transposing reads are issued from inline assembly and completed by
-  // vt_wait(): every one of them reads a stage whose global->LDS loads this
-  // wave has already waited for (the compiler cannot see that and would
-  // otherwise wait for all loads in flight, stalling the prefetch ring).
+  // The sixteen transposing reads and the wait for them are one inline-assembly
+  // statement, so no instruction can see the registers before the data has
+  // arrived. Every read targets a stage whose global->LDS loads this wave has
+  // already waited for; the compiler cannot see that, and with its own
+  // transposing-read builtin it would also wait for the loads still in flight
+  // into the other stages, stalling the prefetch ring.
   auto load_v = [&](const char* vt, uint2* vr, int i0) __attribute__((always_inline)) {
+    uint32_t a[2];
 #pragma unroll
-    for (int i = i0; i < i0 + 2; ++i) {
-      const int vch = ((i * 4 + v_chunk_lo) ^ v_swz<D>(v_row)) * 16 + v_in;
-      const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(vt + v_row * T::kRowBytes + vch);
-      uint2* r = vr + (i - i0) * 8;  // [bb][sub][lo, hi]
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-          "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-          "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-          "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-          "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-          "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-          "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-          "ds_read_b64_tr_b16 %7, %8 offset:%16"
-          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-          : "v"(a), "i"(0 * T::kRowBytes), "i"(8 * T::kRowBytes), "i"(16 * T::kRowBytes), "i"(24 * T::kRowBytes),
-            "i"(32 * T::kRowBytes), "i"(40 * T::kRowBytes), "i"(48 * T::kRowBytes), "i"(56 * T::kRowBytes));
+    for (int il = 0; il < 2; ++il) {
+      const int vch = (((i0 + il) * 4 + v_chunk_lo) ^ v_swz<D>(v_row)) * 16 + v_in;
+      a[il] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(vt + v_row * T::kRowBytes + vch);
     }
-  };
-  // Wait for this wave's outstanding LDS reads; the values pass through the
-  // statement so that nothing reads them earlier.
-  auto vt_wait = [&](uint2* vr) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
-                   "+v"(vr[7]), "+v"(vr[8]), "+v"(vr[9]), "+v"(vr[10]), "+v"(vr[11]), "+v"(vr[12]), "+v"(vr[13]),
-                   "+v"(vr[14]), "+v"(vr[15]));
+    // vr[8 il + m] <- rows 8m .. of d-block i0 + il, i.e. [il][bb][sub][lo, hi]
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %8, %17 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %12, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %14, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %15, %17 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+          "=&v"(vr[14]), "=&v"(vr[15])
+        : "v"(a[0]), "v"(a[1]), "i"(0 * T::kRowBytes), "i"(8 * T::kRowBytes), "i"(16 * T::kRowBytes),
+          "i"(24 * T::kRowBytes), "i"(32 * T::kRowBytes), "i"(40 * T::kRowBytes), "i"(48 * T::kRowBytes),
+          "i"(56 * T::kRowBytes));
   };
   // operand (il, bb, sub) of the d-block pair held in vr
   auto v_operand = [&](const uint2* vr, int il, int bb, int sub) __attribute__((always_inline)) -> bf16x8 {
@@ -472,7 +479,6 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     for (int i0 = 0; i0 < DB; i0 += 2) {
       uint2 vr[16];
       load_v(vt, vr, i0);
-      vt_wait(vr);
 #pragma unroll
       for (int il = 0; il < 2; ++il)
 #pragma unroll
