@@ -414,9 +414,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   // The sixteen transposing reads and the wait for them are one inline-assembly
   // statement, so no instruction can see the registers before the data has
   // arrived. Every read targets a stage whose global->LDS loads this wave has
-  // already waited for; the compiler cannot see that, and with its own
-  // transposing-read builtin it would also wait for the loads still in flight
-  // into the other stages, stalling the prefetch ring.
+  // already waited for. (With the compiler's transposing-read builtin instead,
+  // it issues these reads four at a time, each group followed by a full wait,
+  // which measured slower.)
   auto load_v = [&](const char* vt, uint2* vr, int i0) __attribute__((always_inline)) {
     uint32_t a[2];
 #pragma unroll
