@@ -212,3 +212,23 @@ def test_round_planted_full_size(name, shape):
         a = offs[s]
         assert L[s] == wL and bonus[s] == wbonus, (s, L[s], wL, bonus[s], wbonus)
         assert list(path[a:a + wL + 1]) == wpath
+
+
+def test_walk_maximum_tree_size():
+    """A chain of DT_MAX_TREE_NODES = 1024 nodes accepted to its end (L = 1023)
+    and a 1024-node random tree, in one call."""
+    require_gpu()
+    n, vocab = 1024, 2048
+    chain = gtrees.chain(n)
+    tok = np.arange(n, dtype=np.int32)
+    full = np.full((n, vocab), -1.0, np.float32)
+    full[np.arange(n - 1), tok[1:]] = 5.0  # node i predicts node i + 1's token
+    full[n - 1, 2047] = 5.0                # the bonus token after the last node
+    r = grng.stream(73, "walk-max")
+    p2, t2 = tree("recursive", n, 74, vocab=vocab)
+    lg2 = gten.logits(r, n, vocab)
+    gten.plant(r, lg2, p2, t2, p=0.9, pick="random")
+    offs = np.array([0, n, 2 * n])
+    print("walk maximum tree size", flush=True)
+    L = _check_walk([chain, p2], [tok, t2], np.concatenate([full, lg2]), offs)
+    assert L[0] == n - 1

@@ -316,3 +316,16 @@ def test_round_replays_from_a_hip_graph():
         for a, b in zip(eager, replayed):
             assert torch.equal(a, b), f"replay {rep}"
         assert int(acc.cpu()[0]) > 0
+
+
+@pytest.mark.parametrize("g,d", [(1, 128), (4, 128), (1, 64)])
+def test_maximum_tree_size(g, d):
+    """Trees of DT_MAX_TREE_NODES = 1024 nodes. With one query head per KV head
+    the ancestor masks of a 256-row tile do not fit beside the K/V ring, so the
+    planner falls back to 128-row tiles; with g = 4 the 256-row tiles stay."""
+    require_gpu()
+    n, P = 1024, 100
+    parents, ops = _case([n], [P], 2 * g, 2, d, ["recursive"], seed=71 + g + d, scale=0.5)
+    print(f"maximum tree n={n} P={P} g={g} d={d}", flush=True)
+    out, _ = _run(ops, parents, [n], [P], 2 * g, 2, d)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"n={n} g={g} d={d}")

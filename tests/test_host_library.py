@@ -146,7 +146,8 @@ def test_attention_validation_errors():
         assert lib.dt_tree_attention_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code, name
         assert lib.dt_tree_attention(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 16, None, 0, None) == code, name
     for kw, code in [(dict(offs=[1, 4]), _lib.DT_ERR_SHAPE), (dict(offs=[0, 0]), _lib.DT_ERR_SHAPE),
-                     (dict(offs=[0, 2000]), _lib.DT_ERR_UNSUPPORTED), (dict(plens=[-1]), _lib.DT_ERR_SHAPE)]:
+                     (dict(offs=[0, 2000]), _lib.DT_ERR_UNSUPPORTED), (dict(offs=[0, 1025]), _lib.DT_ERR_UNSUPPORTED),
+                     (dict(plens=[-1]), _lib.DT_ERR_SHAPE)]:
         d, keep = _desc(**kw)
         assert lib.dt_tree_attention_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code, kw
     d, keep = _desc()
