@@ -993,6 +993,31 @@ int64_t choose_chunk(const dt_attn_desc* d, int g, int rm, int cus) {
   return std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
 }
 
+// Sequences whose key counts differ (a ragged batch) make units of unequal
+// length: sized for one workgroup per CU, the chunks would leave the CUs that
+// drew short units idle while long ones finish. There the chunks are sized for
+// about three workgroups per CU (at least 16 tiles), which the dispatcher
+// balances as workgroups finish.
+bool ragged_keys(const dt_attn_desc* d) {
+  for (int s = 1; s < d->num_seqs; ++s)
+    if ((int64_t)d->prefix_lens[s] + (d->node_offsets[s + 1] - d->node_offsets[s]) !=
+        (int64_t)d->prefix_lens[0] + (d->node_offsets[1] - d->node_offsets[0]))
+      return true;
+  return false;
+}
+
+int64_t choose_chunk_ragged(const dt_attn_desc* d, int g, int rm, int cus) {
+  int64_t total_tiles = 0, max_keys = 0;
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int n = d->node_offsets[s + 1] - d->node_offsets[s];
+    const int64_t keys = (int64_t)d->prefix_lens[s] + n;
+    total_tiles += ceil_div((int64_t)n * g, rm) * d->num_kv_heads * ceil_div(keys, kBN);
+    max_keys = std::max(max_keys, keys);
+  }
+  const int64_t tiles = std::max<int64_t>(16, ceil_div(total_tiles, 3 * (int64_t)cus));
+  return std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
+}
+
 bool needs_split(const dt_attn_desc* d, int64_t chunk) {
   for (int s = 0; s < d->num_seqs; ++s)
     if ((int64_t)d->prefix_lens[s] + (d->node_offsets[s + 1] - d->node_offsets[s]) > chunk) return true;
@@ -1018,11 +1043,12 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   // splitting the keys where 256 would need it (e.g. ragged prefixes); fewer
   // rows when the trees are small or the ancestor masks do not fit the LDS.
   int wm = choose_wm(d, g);
+  const bool ragged = !d->split_keys && ragged_keys(d);
   // 128-row tiles instead of 256-row ones when that avoids the key split, or
   // when the split would leave each workgroup at most eight steps: there the
   // split partials' round trip (written by every chunk, read back by the
   // merge) costs more than the shorter tiles, and 128-row tiles halve it.
-  if (wm == 8 && !d->split_keys && lds_fits(D, 4, max_n, g)) {
+  if (wm == 8 && !d->split_keys && !ragged && lds_fits(D, 4, max_n, g)) {
     const int64_t chunk8 = choose_chunk(d, g, kWaveRows * 8, cus);
     if (needs_split(d, chunk8) &&
         (!needs_split(d, choose_chunk(d, g, kWaveRows * 4, cus)) || chunk8 <= 8 * kBN))
@@ -1032,7 +1058,7 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   if (!lds_fits(D, wm, max_n, g)) return DT_ERR_UNSUPPORTED;
   plan->wm = wm;
   const int rm = kWaveRows * wm;
-  int64_t chunk = choose_chunk(d, g, rm, cus);
+  int64_t chunk = ragged && wm == 8 ? choose_chunk_ragged(d, g, rm, cus) : choose_chunk(d, g, rm, cus);
   if (chunk > (int64_t)1 << 30) chunk = (int64_t)1 << 30;
 
   size_t part_rows = 0;
