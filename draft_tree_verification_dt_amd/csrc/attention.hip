@@ -993,17 +993,20 @@ int64_t choose_chunk(const dt_attn_desc* d, int g, int rm, int cus) {
   return std::min(tiles * kBN, ceil_div(max_keys, kBN) * kBN);
 }
 
-// Sequences whose key counts differ (a ragged batch) make units of unequal
-// length: sized for one workgroup per CU, the chunks would leave the CUs that
-// drew short units idle while long ones finish. There the chunks are sized for
+// Sequences whose key counts differ widely (a ragged batch: the longest has
+// more than 1.5 times the keys of the shortest) make units of unequal length:
+// sized for one workgroup per CU, the chunks would leave the CUs that drew
+// short units idle while long ones finish. There the chunks are sized for
 // about three workgroups per CU (at least 16 tiles), which the dispatcher
-// balances as workgroups finish.
+// balances as workgroups finish. Nearly equal lengths keep the one-wave plan.
 bool ragged_keys(const dt_attn_desc* d) {
-  for (int s = 1; s < d->num_seqs; ++s)
-    if ((int64_t)d->prefix_lens[s] + (d->node_offsets[s + 1] - d->node_offsets[s]) !=
-        (int64_t)d->prefix_lens[0] + (d->node_offsets[1] - d->node_offsets[0]))
-      return true;
-  return false;
+  int64_t lo = INT64_MAX, hi = 0;
+  for (int s = 0; s < d->num_seqs; ++s) {
+    const int64_t keys = (int64_t)d->prefix_lens[s] + (d->node_offsets[s + 1] - d->node_offsets[s]);
+    lo = std::min(lo, keys);
+    hi = std::max(hi, keys);
+  }
+  return 2 * hi > 3 * lo;
 }
 
 int64_t choose_chunk_ragged(const dt_attn_desc* d, int g, int rm, int cus) {
