@@ -1042,9 +1042,11 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   int max_n = 1;
   for (int s = 0; s < d->num_seqs; ++s) max_n = std::max(max_n, d->node_offsets[s + 1] - d->node_offsets[s]);
 
-  // 256 rows per workgroup (the ping-pong schedule) unless 128 rows avoid
-  // splitting the keys where 256 would need it (e.g. ragged prefixes); fewer
-  // rows when the trees are small or the ancestor masks do not fit the LDS.
+  // 256 rows per workgroup (the ping-pong schedule) unless, in a batch of
+  // (nearly) equal lengths, 128 rows avoid splitting the keys where 256 would
+  // need it; fewer rows when the trees are small or the ancestor masks do not
+  // fit the LDS. A ragged batch keeps 256-row tiles and balances through
+  // smaller key chunks.
   int wm = choose_wm(d, g);
   const bool ragged = !d->split_keys && ragged_keys(d);
   // 128-row tiles instead of 256-row ones when that avoids the key split, or
