@@ -329,3 +329,34 @@ def test_maximum_tree_size(g, d):
     print(f"maximum tree n={n} P={P} g={g} d={d}", flush=True)
     out, _ = _run(ops, parents, [n], [P], 2 * g, 2, d)
     assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"n={n} g={g} d={d}")
+
+
+@pytest.mark.parametrize("n,P", [(48, 300), (300, 700)])
+def test_relabelling_permutes_outputs(n, P):
+    """A random topological renumbering of the same tree (nodes, their Q/K/V and
+    parents permuted together) permutes the outputs: node i's attention depends
+    on its ancestors, not on their numbering. The tree keys then arrive in
+    another order, so the comparison is at the attention tolerance; both runs
+    are also checked against the oracle."""
+    require_gpu()
+    parents, ops = _case([n], [P], 8, 2, 128, ["recursive"], seed=81 + n, scale=0.8)
+    parent = parents[0]
+    r = grng.stream(82, "relabel", n)
+    placed, order = {0}, [0]
+    while len(order) < n:
+        ready = [i for i in range(n) if i not in placed and parent[i] in placed]
+        i = ready[int(r.integers(0, len(ready)))]
+        placed.add(i)
+        order.append(i)
+    new_of = {old: new for new, old in enumerate(order)}
+    parent2 = np.array([-1 if old == 0 else new_of[int(parent[old])] for old in order], np.int32)
+    ops2 = dict(ops)
+    for key in ("q", "k_tree", "v_tree"):
+        ops2[key] = ops[key][order]
+    print(f"relabelling n={n} P={P}", flush=True)
+    base, _ = _run(ops, [parent], [n], [P], 8, 2, 128)
+    got, _ = _run(ops2, [parent2], [n], [P], 8, 2, 128)
+    b, g2 = host_f64(base), host_f64(got)
+    assert_attention_close(g2, b[order], what=f"relabelled n={n}")
+    assert_attention_close(b, _oracle(ops, [parent], [n], [P]), what=f"original n={n}")
+    assert_attention_close(g2, _oracle(ops2, [parent2], [n], [P]), what=f"relabelled vs oracle n={n}")
