@@ -360,3 +360,34 @@ def test_relabelling_permutes_outputs(n, P):
     assert_attention_close(g2, b[order], what=f"relabelled n={n}")
     assert_attention_close(b, _oracle(ops, [parent], [n], [P]), what=f"original n={n}")
     assert_attention_close(g2, _oracle(ops2, [parent2], [n], [P]), what=f"relabelled vs oracle n={n}")
+
+
+@pytest.mark.parametrize("n,P", [(100, 500), (16, 1200)])
+def test_fused_qkv_views_and_strided_output(n, P):
+    """Q, K and V as column slices of one fused projection output [N, (Hq + 2 Hkv) d]
+    (row strides larger than their own width) and the output written into a
+    slice of a wider buffer: the same result as contiguous operands, and the
+    columns around the output slice untouched."""
+    import torch
+
+    require_gpu()
+    Hq, Hkv, d = 8, 2, 128
+    parents, ops = _case([n], [P], Hq, Hkv, d, ["recursive"], seed=91 + n, scale=0.6)
+    qkv = torch.cat([dev_bf16(ops["q"]).reshape(n, Hq * d), dev_bf16(ops["k_tree"]).reshape(n, Hkv * d),
+                     dev_bf16(ops["v_tree"]).reshape(n, Hkv * d)], dim=1).contiguous()
+    q = qkv[:, :Hq * d].view(n, Hq, d)
+    kt = qkv[:, Hq * d:(Hq + Hkv) * d].view(n, Hkv, d)
+    vt = qkv[:, (Hq + Hkv) * d:].view(n, Hkv, d)
+    assert q.stride(0) == (Hq + 2 * Hkv) * d and kt.stride() == vt.stride()
+    kp, vp = dev_bf16(ops["k_prefix"]), dev_bf16(ops["v_prefix"])
+    par = dev_i32(parents[0])
+    layout = dt.AttnLayout([0, n], [P])
+    wide = torch.full((n, (Hq + 3) * d), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = wide[:, d:(Hq + 1) * d].view(n, Hq, d)
+    print(f"fused qkv n={n} P={P}", flush=True)
+    dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, out=out)
+    ref_dev = dt.dt_tree_attention(q.contiguous(), kt.contiguous(), vt.contiguous(), kp, vp, par, layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_dev), "strided operands changed the result"
+    assert bool((wide[:, :d] == 7.0).all()) and bool((wide[:, (Hq + 1) * d:] == 7.0).all()), "wrote outside the slice"
+    assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"fused qkv n={n}")
