@@ -35,7 +35,7 @@ def _planted_walk(r, nodes, vocab=64, shapes=("recursive", "deep", "chain"), pla
 
 
 def _run_commit(seed, nodes, plens, layers, Hkv, d, head_major=False, max_path=0, gap=5,
-                shapes=("recursive", "deep", "chain"), plant_p=0.9):
+                shapes=("recursive", "deep", "chain"), plant_p=0.9, fused_tree=False):
     import torch
 
     r = grng.stream(seed, "commit-gpu")
@@ -50,6 +50,12 @@ def _run_commit(seed, nodes, plens, layers, Hkv, d, head_major=False, max_path=0
     path, acc, _ = dt.dt_accept_path(offs, dev_i32(np.concatenate(parents)), dev_i32(np.concatenate(tokens)), am)
     kt = [dev_bf16(gten.normal_bf16(r, (N, Hkv, d))) for _ in range(layers)]
     vt = [dev_bf16(gten.normal_bf16(r, (N, Hkv, d))) for _ in range(layers)]
+    if fused_tree:  # tree K/V as column slices of a fused [N, (4 Hkv + 2 Hkv) d] projection output
+        fused = [torch.cat([torch.zeros((N, 4 * Hkv * d), dtype=torch.bfloat16, device="cuda"),
+                            k.reshape(N, Hkv * d), v.reshape(N, Hkv * d)], dim=1).contiguous()
+                 for k, v in zip(kt, vt)]
+        kt = [f[:, 4 * Hkv * d:5 * Hkv * d].view(N, Hkv, d) for f in fused]
+        vt = [f[:, 5 * Hkv * d:].view(N, Hkv, d) for f in fused]
     host_kc = [gten.normal_bf16(r, (total, Hkv, d)) for _ in range(layers)]
     host_vc = [gten.normal_bf16(r, (total, Hkv, d)) for _ in range(layers)]
     if head_major:  # [Hkv][rows][d] storage viewed as [rows][Hkv][d]
@@ -85,6 +91,13 @@ def test_commit_ragged_batches(seed):
     plens = [int(r.integers(0, 300)) for _ in range(S)]
     acc = _run_commit(seed, nodes, plens, layers=3, Hkv=[1, 2, 8][seed], d=[64, 128, 128][seed])
     assert acc.max() > 0
+
+
+def test_commit_from_fused_projection_rows():
+    """Tree K/V read from slices of a fused QKV projection output (row stride
+    6 Hkv d instead of Hkv d)."""
+    require_gpu()
+    _run_commit(13, [60, 25], [100, 333], layers=2, Hkv=2, d=128, fused_tree=True)
 
 
 def test_commit_head_major_cache():
