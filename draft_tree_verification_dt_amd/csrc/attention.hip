@@ -458,16 +458,22 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   };
   static_assert(DB % 2 == 0, "d-blocks come in pairs");
 
-  // S(step): both 32-key blocks; one K block in registers at a time.
+  // S(step): both 32-key blocks; one K block in registers at a time. Each
+  // operand of the second block is read into the register of the first
+  // block's operand that the product just issued has consumed, so those reads
+  // overlap the first block's products.
   auto s_product = [&](const char* kt) __attribute__((always_inline)) {
     bf16x8 ka[KS];
     load_k(kt, ka, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
+    for (int k = 0; k < KS; ++k) {
       sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k], qreg[k], k ? sc[0] : f32x16{}, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(kt, ka, 1);
+      const int chunk = (2 * k + hh) ^ k_swz<D>(lr);
+      ka[k] = *reinterpret_cast<const bf16x8*>(kt + 32 * T::kRowBytes + k_off + chunk * 16);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product,
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < KS; ++k)
@@ -597,7 +603,10 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     // SIMD's matrix core is fed by one of its two waves while the other works
     // on the VALU. Group B trails group A by one phase. Tile s is read from
     // phase 2s (A's S) to phase 2s + 3 (B's PV); its stage is refilled with
-    // tile s + 4 at phase 2s + 4, and each tile is loaded two steps ahead.
+    // tile s + 4 from phase 2s + 4 on, and each tile is loaded two steps ahead.
+    // Each group requests its share of a tile at the start of its own softmax
+    // phase (B in phase 2s, A in phase 2s + 1), so only four waves contend for
+    // the address unit at a time and the MFMA blocks start without it.
     const bool grp_b = wave >= 4;
     auto x_block = [&](int s, Stage cur, Stage prev) __attribute__((always_inline)) {
       if (!wave_active) return;
@@ -605,13 +614,13 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       s_product(cur.k);
     };
     // even phase of step s: tile s must have landed (tile s + 1 may still be
-    // in flight); after the barrier, tile s + 2 is requested
+    // in flight); after the barrier, group B requests its share of tile s + 2
     auto even_barrier = [&](int s, auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       if (s + 1 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       stage_barrier();
-      if (s + 2 < nsteps) issue(key_lo + (s + 2) * KN, stage_ptr(std::integral_constant<int, (u + 2) % 4>{}));
+      if (grp_b && s + 2 < nsteps) issue(key_lo + (s + 2) * KN, stage_ptr(std::integral_constant<int, (u + 2) % 4>{}));
     };
     // The two groups run separate copies of the loop (so that S and P are
     // never both live across a barrier) with the same sequence of barriers.
@@ -620,6 +629,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       even_barrier(s, U);
       x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
       stage_barrier();
+      if (s + 2 < nsteps) issue(key_lo + (s + 2) * KN, stage_ptr(std::integral_constant<int, (u + 2) % 4>{}));
       if (wave_active) softmax(s);
     };
     auto group_b = [&](int s, auto U) __attribute__((always_inline)) {
