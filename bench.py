@@ -45,6 +45,8 @@ def parse():
                     help="independent per-layer KV caches the step cycles through (0: the workload's own; "
                          "enough of them keep one workload's caches out of the 256 MB last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the attention-only timings of the b128, ragged and long workloads")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="0: greedy verification (dt_argmax_rows); > 0: exact target-sample matching (dt_sample_rows)")
@@ -370,6 +372,83 @@ def time_small_tree(rnd, reps=40, n=16):
     return ms, nbytes, flops
 
 
+OTHER_WORKLOADS = (("b128", 40), ("ragged", 6), ("long", 3))  # (workload, rotating layer caches)
+
+
+def time_attention_workload(rnd, name, layers, reps=3):
+    """dt_tree_attention alone on another workload's geometry: its own trees
+    (best-first over its candidate tables), operands drawn on the device, and
+    `layers` independent KV caches that the calls rotate through so that the
+    prefix streams from HBM. Mean call time from one pair of HIP events around
+    reps x layers calls on the library's stream (two round calls are queued
+    ahead so the host has enqueued the calls before the GPU reaches them); the
+    roofline object of that call."""
+    import ctypes
+
+    from gen import configs as gconf, draft as gdraft, rng as grng, tensors as gten
+    from oracle.attention import flops as att_flops
+
+    torch, dt = rnd.torch, rnd.dt
+    w = gconf.get(name)
+    w.layers = layers
+    N, CR, Hq, Hkv, d = w.total_nodes, w.total_cache_rows, w.Hq, w.Hkv, w.d
+    sc = 1.0 / np.sqrt(d)
+    parents = []
+    for s, n in enumerate(w.nodes):
+        r = grng.stream(w.seed, "cand", 0, s)
+        lp, tok = gdraft.candidates(r, depths=w.depths, vocab=w.vocab, k=w.cand_k(n))
+        parents.append(dt.dt_build_tree(lp, tok, int(r.integers(0, w.vocab)), n, with_score=False)[0])
+    par = torch.from_numpy(np.concatenate(parents).astype(np.int32)).to(rnd.dev)
+    layout = dt.AttnLayout(w.node_offsets(), w.prefix_lens, w.cache_row_starts())
+    kp = [gten.device_randn_bf16((CR, Hkv, d), w.seed, "kp", l, scale=sc) for l in range(layers)]
+    vp = [gten.device_randn_bf16((CR, Hkv, d), w.seed, "vp", l, scale=sc) for l in range(layers)]
+    q = [gten.device_randn_bf16((N, Hq, d), w.seed, "q", l, scale=sc) for l in range(layers)]
+    kt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "kt", l, scale=sc) for l in range(layers)]
+    vt = [gten.device_randn_bf16((N, Hkv, d), w.seed, "vt", l, scale=sc) for l in range(layers)]
+    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=rnd.dev)
+    desc = dt._attn_geometry(q[0], kt[0], kp[0], layout, None, 0)
+    desc.out_row_stride = out.stride(0)
+    ws = torch.empty(max(dt.dt_tree_attention_workspace_size(q[0], kt[0], kp[0], layout), 256), dtype=torch.uint8,
+                     device=rnd.dev)
+    dref = ctypes.byref(desc)
+
+    def call(l):
+        st = rnd.lib.dt_tree_attention(dref, q[l].data_ptr(), kt[l].data_ptr(), vt[l].data_ptr(), kp[l].data_ptr(),
+                                       vp[l].data_ptr(), par.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       rnd.stream)
+        if st != 0:
+            raise dt.DtError(st, "dt_tree_attention")
+
+    for l in range(layers):
+        call(l)  # first touch of every cache, and the code object
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rnd.attention(0)
+    rnd.attention(1 % rnd.w.layers)
+    a.record()
+    for i in range(reps * layers):
+        call(i % layers)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * layers)
+    fl = float(att_flops(w.nodes, w.prefix_lens, parents, Hq, d))
+    nbytes = attention_bytes(w)
+    res = {"workload": w.name, "num_seqs": w.num_seqs, "tree_nodes": w.nodes[0] if len(set(w.nodes)) == 1 else w.nodes,
+           "prefix_lens": w.prefix_lens, "us": round(ms * 1e3, 2), "calls_timed": reps * layers,
+           "layer_caches": layers, "flops_per_launch": fl, "algorithmic_bytes_per_launch": nbytes}
+    if fl / nbytes >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        tf = fl / (ms / 1e3) / 1e12
+        res.update({"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+    else:
+        gbs = nbytes / (ms / 1e3) / 1e9
+        res.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    del kp, vp, q, kt, vt
+    torch.cuda.empty_cache()
+    return res
+
+
 class DraftBuild:
     """DARTree's construction kernels at the pages' pruned configuration: gamma = 16
     draft positions over the vocabulary, K = 64 candidates, width W = 12, beta =
@@ -642,6 +721,9 @@ def main():
     com_ms, com_bytes, com_acc = time_commit_calls(rnd, reps=10)
     db, draft = time_draft_build(rnd)
     graph_ms = time_round_graph(rnd)
+    others = None
+    if w.name == gconf.qwen_b256_round().name and not args.no_other_workloads:
+        others = {name: time_attention_workload(rnd, name, layers) for name, layers in OTHER_WORKLOADS}
     small = None
     if w.num_seqs == 1:
         ch_ms, ch_bytes, ch_flops = time_small_tree(rnd)
@@ -687,6 +769,7 @@ def main():
         "commit": {"kernel": "dt_commit_kv, all layers in one call", "us": com_ms * 1e3, "bytes": com_bytes,
                    "GB/s": com_bytes / (com_ms / 1e3) / 1e9, "accept_len": com_acc.tolist()},
         "small_tree": small,
+        "other_workloads": others,
         "draft_tree": dict(draft, kernels="dt_topk_rows, dt_expand_depth (x16 in the chain), dt_prune_topb"),
         "step_variant": {"temperature": args.temperature, "commit": bool(args.commit)},
         "parity": None,

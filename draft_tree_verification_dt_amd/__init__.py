@@ -132,6 +132,34 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _req(t, name, dtype, device=None, min_len=None, flat=False):
+    """Check a device argument before its pointer reaches the library, which
+    cannot check dtypes, devices or extents itself: a torch CUDA tensor of
+    ``dtype`` (on ``device`` when given), with at least ``min_len`` entries along
+    its first dimension; ``flat`` asks for a unit-stride 1-D view of them.
+    Returns the tensor's device."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a CUDA tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, other operands on {device}")
+    if flat and (t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1)):
+        raise ValueError(f"{name}: expected a contiguous 1-D tensor")
+    if min_len is not None and (t.dim() == 0 or t.shape[0] < min_len):
+        raise ValueError(f"{name}: needs at least {min_len} entries, has {t.shape[0] if t.dim() else 0}")
+    return t.device
+
+
+def _req_workspace(ws, name, device):
+    if ws is not None:
+        _req(ws, name, ws.dtype, device)
+        if not ws.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+
+
 def _desc(layout, Hq, Hkv, d, scale, split_keys, q_rs, out_rs, tree_rs, p_rs, p_hs):
     desc = dt_attn_desc()
     desc.num_seqs = layout.num_seqs
@@ -185,13 +213,42 @@ def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, sca
     """
     import torch
 
+    bf = torch.bfloat16
+    dev = _req(q, "q", bf)
+    if q.dim() != 3 or k_tree.dim() != 3 or tuple(k_tree.shape) != tuple(v_tree.shape):
+        raise ValueError("q [N, Hq, d]; k_tree and v_tree [N, Hkv, d] of one shape")
+    N, Hq, d = q.shape
+    if k_tree.shape[0] != N or k_tree.shape[2] != d:
+        raise ValueError("k_tree/v_tree must have q's rows and head_dim")
+    _req(k_tree, "k_tree", bf, dev)
+    _req(v_tree, "v_tree", bf, dev)
+    if int(layout.node_offsets[-1]) != N:
+        raise ValueError(f"layout covers {int(layout.node_offsets[-1])} rows, q has {N}")
+    _req(parent, "parent", torch.int32, dev, N, flat=True)
+    if (k_prefix is None) != (v_prefix is None):
+        raise ValueError("k_prefix and v_prefix are both given or both None")
+    if k_prefix is not None:
+        _req(k_prefix, "k_prefix", bf, dev)
+        _req(v_prefix, "v_prefix", bf, dev)
+        if k_prefix.dim() != 3 or tuple(k_prefix.shape) != tuple(v_prefix.shape) or \
+                tuple(k_prefix.shape[1:]) != tuple(k_tree.shape[1:]):
+            raise ValueError("k_prefix/v_prefix: [rows, Hkv, d] of one shape, heads and d as k_tree")
+        ends = layout.prefix_row_start + layout.prefix_lens.astype(np.int64)
+        if len(ends) and int(ends.max()) > k_prefix.shape[0]:
+            raise ValueError(f"a prefix ends at row {int(ends.max())}, the cache has {k_prefix.shape[0]} rows")
+    elif (layout.prefix_lens > 0).any():
+        raise ValueError("non-empty prefixes need k_prefix and v_prefix")
     if k_prefix is not None and (k_prefix.stride() != v_prefix.stride()):
         raise ValueError("k_prefix and v_prefix must share strides")
     if k_tree.stride() != v_tree.stride():
         raise ValueError("k_tree and v_tree must share strides")
     desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=bf, device=dev)
+    _req(out, "out", bf, dev)
+    if tuple(out.shape) != tuple(q.shape) or out.stride(2) != 1 or (Hq > 1 and out.stride(1) != d):
+        raise ValueError("out: [N, Hq, d] like q, with contiguous heads")
+    _req_workspace(workspace, "workspace", dev)
     desc.out_row_stride = _row_stride(out, q.shape[1] * q.shape[2])
     lib = _lib.load()
     need = ctypes.c_size_t(0)
@@ -221,11 +278,16 @@ def dt_argmax_rows(logits, out=None, workspace=None, stream=None):
     with unit column stride. Returns int32 [rows]."""
     import torch
 
+    dev = _req(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [rows, vocab]")
     rows, vocab = logits.shape
     if logits.stride(1) != 1:
         raise ValueError("logits: vocab dimension must be contiguous")
     if out is None:
-        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        out = torch.empty(rows, dtype=torch.int32, device=dev)
+    _req(out, "out", torch.int32, dev, rows, flat=True)
+    _req_workspace(workspace, "workspace", dev)
     need = dt_argmax_rows_workspace_size(rows, vocab)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
@@ -250,11 +312,16 @@ def dt_sample_rows(logits, temperature, seed, offset, out=None, workspace=None, 
     [rows, vocab] float32 CUDA tensor with unit column stride. Returns int32 [rows]."""
     import torch
 
+    dev = _req(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [rows, vocab]")
     rows, vocab = logits.shape
     if logits.stride(1) != 1:
         raise ValueError("logits: vocab dimension must be contiguous")
     if out is None:
-        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        out = torch.empty(rows, dtype=torch.int32, device=dev)
+    _req(out, "out", torch.int32, dev, rows, flat=True)
+    _req_workspace(workspace, "workspace", dev)
     need = dt_sample_rows_workspace_size(rows, vocab)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
@@ -274,13 +341,19 @@ def dt_accept_path(node_offsets, parent, token, argmax_idx, path=None, accept_le
 
     offs = _i32(node_offsets)
     S = len(offs) - 1
-    dev = parent.device
+    N = int(offs[-1]) if S >= 1 else 0
+    dev = _req(parent, "parent", torch.int32, None, N, flat=True)
+    _req(token, "token", torch.int32, dev, N, flat=True)
+    _req(argmax_idx, "argmax_idx", torch.int32, dev, N, flat=True)
     if path is None:
-        path = torch.empty(parent.shape[0], dtype=torch.int32, device=dev)
+        path = torch.empty(max(parent.shape[0], N), dtype=torch.int32, device=dev)
     if accept_len is None:
         accept_len = torch.empty(S, dtype=torch.int32, device=dev)
     if bonus is None:
         bonus = torch.empty(S, dtype=torch.int32, device=dev)
+    _req(path, "path", torch.int32, dev, N, flat=True)
+    _req(accept_len, "accept_len", torch.int32, dev, S, flat=True)
+    _req(bonus, "bonus", torch.int32, dev, S, flat=True)
     st = _lib.load().dt_accept_path(S, _ptr(offs, ctypes.c_int32), parent.data_ptr(), token.data_ptr(),
                                     argmax_idx.data_ptr(), path.data_ptr(), accept_len.data_ptr(), bonus.data_ptr(),
                                     _stream(stream))
@@ -304,8 +377,23 @@ class CommitArgs:
         L = len(k_tree)
         if not (len(v_tree) == len(k_cache) == len(v_cache) == L) or L < 1:
             raise ValueError("one tree K/V and cache K/V tensor per layer")
+        import torch
+
         kt0, kc0 = k_tree[0], k_cache[0]
+        dev = _req(kt0, "k_tree[0]", torch.bfloat16)
+        for name, ts in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache), ("v_cache", v_cache)):
+            for i, t in enumerate(ts):
+                _req(t, f"{name}[{i}]", torch.bfloat16, dev)
+                if t.dim() != 3:
+                    raise ValueError(f"{name}[{i}]: expected [rows, Hkv, d]")
         _, Hkv, d = kt0.shape
+        N = int(layout.node_offsets[-1])
+        for t in list(k_tree) + list(v_tree):
+            if tuple(t.shape) != tuple(kt0.shape) or t.shape[0] < N:
+                raise ValueError(f"tree K/V: [N >= {N}, Hkv, d], all layers alike")
+        for t in list(k_cache) + list(v_cache):
+            if tuple(t.shape[1:]) != (Hkv, d):
+                raise ValueError("cache K/V: [rows, Hkv, d] with the tree's heads and head_dim")
         for t in list(k_tree) + list(v_tree):
             if t.stride() != kt0.stride() or t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != d):
                 raise ValueError("tree K/V: [rows][heads][d] with contiguous heads, all layers alike")
@@ -316,6 +404,11 @@ class CommitArgs:
         self.cache_rows = np.ascontiguousarray(cache_rows, dtype=np.int64)
         if len(self.cache_rows) != layout.num_seqs:
             raise ValueError("cache_rows needs one entry per sequence")
+        ends = layout.prefix_row_start + self.cache_rows
+        if len(ends) and int(ends.max()) > min(t.shape[0] for t in list(k_cache) + list(v_cache)):
+            raise ValueError("a sequence's cache room ends past the cache's last row")
+        self.device = dev
+        self.num_nodes = N
         desc = _lib.dt_commit_desc()
         desc.num_seqs = layout.num_seqs
         desc.num_layers = L
@@ -342,6 +435,10 @@ def dt_commit_kv(args, path, accept_len, stream=None):
     """Copy every layer's accepted-path K/V rows into the cache (GPU). ``args``:
     CommitArgs; path int32 [N] and accept_len int32 [S] CUDA tensors as
     dt_accept_path leaves them."""
+    import torch
+
+    _req(path, "path", torch.int32, args.device, args.num_nodes, flat=True)
+    _req(accept_len, "accept_len", torch.int32, args.device, args.layout.num_seqs, flat=True)
     st = _lib.load().dt_commit_kv(ctypes.byref(args.desc), args.k_tree, args.v_tree, args.k_cache, args.v_cache,
                                   path.data_ptr(), accept_len.data_ptr(), _stream(stream))
     _check(st, "dt_commit_kv")
@@ -360,14 +457,19 @@ def dt_topk_rows(logits, k, out_token=None, out_logprob=None, workspace=None, st
     log-softmax values. Returns (tokens int32 [rows, k], logprob float32 [rows, k])."""
     import torch
 
+    dev = _req(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [rows, vocab]")
     rows, vocab = logits.shape
     if logits.stride(1) != 1:
         raise ValueError("logits: vocab dimension must be contiguous")
-    dev = logits.device
     if out_token is None:
         out_token = torch.empty((rows, k), dtype=torch.int32, device=dev)
     if out_logprob is None:
         out_logprob = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    _req(out_token, "out_token", torch.int32, dev)
+    _req(out_logprob, "out_logprob", torch.float32, dev)
+    _req_workspace(workspace, "workspace", dev)
     for t in (out_token, out_logprob):
         if not t.is_contiguous() or tuple(t.shape) != (rows, k):
             raise ValueError("outputs must be contiguous [rows, k]")
@@ -388,16 +490,27 @@ def dt_expand_depth(parent_score, child_logq, cand_token, w, beta, out=None, str
     stride (e.g. views of a [S, depths, w] supertree). Returns that tuple."""
     import torch
 
+    dev = _req(child_logq, "child_logq", torch.float32)
+    if child_logq.dim() != 3 or parent_score.dim() != 2 or cand_token.dim() != 2:
+        raise ValueError("parent_score [S, w_prev], child_logq [S, w_prev, k], cand_token [S, k]")
     S, w_prev, k = child_logq.shape
+    _req(parent_score, "parent_score", torch.float32, dev, S)
+    _req(cand_token, "cand_token", torch.int32, dev, S)
+    if parent_score.shape[1] < w_prev or cand_token.shape[1] < k:
+        raise ValueError("parent_score needs w_prev columns and cand_token k columns")
     if child_logq.stride(2) != 1 or (w_prev > 1 and child_logq.stride(1) != k):
         raise ValueError("child_logq: each sequence's [w_prev, k] block must be contiguous")
     for t in (parent_score, cand_token):
         if t.shape[1] > 1 and t.stride(1) != 1:
             raise ValueError("parent_score / cand_token rows must be contiguous")
-    dev = child_logq.device
     if out is None:
         out = (torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.int32, device=dev),
                torch.empty((S, w), dtype=torch.int32, device=dev), torch.empty((S, w), dtype=torch.float32, device=dev))
+    for t, name, ty in zip(out, ("sel_parent", "sel_cand", "sel_token", "sel_score"),
+                           (torch.int32, torch.int32, torch.int32, torch.float32)):
+        _req(t, name, ty, dev, S)
+        if t.dim() != 2 or t.shape[1] < w:
+            raise ValueError(f"{name}: expected [S, w]")
     rs = _row_stride(out[0], w)
     if any(_row_stride(t, w) != rs or (w > 1 and t.stride(1) != 1) for t in out):
         raise ValueError("outputs must share one row stride with contiguous rows")
@@ -416,16 +529,27 @@ def dt_prune_topb(sel_parent, sel_token, sel_score, root_token, budget, out=None
     score) [S, budget + 1] and n_out [S]."""
     import torch
 
+    dev = _req(sel_parent, "sel_parent", torch.int32)
+    if sel_parent.dim() != 3:
+        raise ValueError("sel_parent: expected [S, depths, w]")
     S, depths, w = sel_parent.shape
+    _req(sel_token, "sel_token", torch.int32, dev)
+    _req(sel_score, "sel_score", torch.float32, dev)
+    _req(root_token, "root_token", torch.int32, dev, S, flat=True)
     for t in (sel_parent, sel_token, sel_score):
         if not t.is_contiguous() or tuple(t.shape) != (S, depths, w):
             raise ValueError("supertree arrays must be contiguous [S, depths, w]")
-    dev = sel_parent.device
     n = int(budget) + 1
     if out is None:
         out = (torch.empty((S, n), dtype=torch.int32, device=dev), torch.empty((S, n), dtype=torch.int32, device=dev),
                torch.empty((S, n), dtype=torch.int32, device=dev), torch.empty((S, n), dtype=torch.float32, device=dev),
                torch.empty(S, dtype=torch.int32, device=dev))
+    for t, name, ty in zip(out, ("parent", "token", "depth", "score", "n_out"),
+                           (torch.int32, torch.int32, torch.int32, torch.float32, torch.int32)):
+        _req(t, name, ty, dev, S)
+        if not t.is_contiguous() or (name != "n_out" and tuple(t.shape) != (S, n)):
+            raise ValueError(f"{name}: expected a contiguous [S, {n}] tensor" if name != "n_out" else
+                             "n_out: expected a contiguous [S] tensor")
     st = _lib.load().dt_prune_topb(S, depths, w, int(budget), sel_parent.data_ptr(), sel_token.data_ptr(),
                                    sel_score.data_ptr(), root_token.data_ptr(), *[t.data_ptr() for t in out],
                                    _stream(stream))

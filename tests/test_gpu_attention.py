@@ -213,9 +213,11 @@ def test_full_size_ragged_batch():
     assert_attention_close(host_f64(out), _oracle(ops, parents, w.nodes, w.prefix_lens), what=w.name)
 
 
-def test_long_context_sampled_rows():
-    """4 x (P=32768, n=512): operands drawn on the device, 96 sampled
-    (sequence, node, head) rows checked against the oracle's per-row form."""
+def test_long_context_full_output():
+    """4 x (P=32768, n=512), one layer: operands drawn on the device, the whole
+    output (4 x 512 nodes x 32 heads) compared with the oracle sequence by
+    sequence. No key split happens at this size: 256 workgroups of 256 rows
+    each stream all 33280 keys of their sequence."""
     import torch
 
     require_gpu()
@@ -234,15 +236,13 @@ def test_long_context_sampled_rows():
     out = dt.dt_tree_attention(q, kt, vt, kp, vp, dev_i32(np.concatenate(parents)), layout)
     torch.cuda.synchronize()
     hq, hkt, hvt, hout = (host_f64(t) for t in (q, kt, vt, out))
-    rng = grng.stream(w.seed, "rows")
     offs, starts = w.node_offsets(), w.prefix_row_starts()
     for s in range(w.num_seqs):
         a, b, p0, P = offs[s], offs[s + 1], starts[s], w.prefix_lens[s]
-        hkp, hvp = host_f64(kp[p0:p0 + P]), host_f64(vp[p0:p0 + P])
-        rows = [(int(rng.integers(0, b - a)), int(rng.integers(0, Hq))) for _ in range(24)]
-        ref = oatt.tree_attention_rows(hq[a:b], hkt[a:b], hvt[a:b], hkp, hvp, parents[s], rows)
-        got = np.stack([hout[a + i, h] for i, h in rows])
-        assert_attention_close(got, ref, what=f"long seq {s}")
+        ref = oatt.tree_attention(hq[a:b], hkt[a:b], hvt[a:b], host_f64(kp[p0:p0 + P]), host_f64(vp[p0:p0 + P]),
+                                  parents[s])
+        print(f"long seq {s} checked", flush=True)
+        assert_attention_close(hout[a:b], ref, what=f"long seq {s}")
 
 
 def test_round_replays_from_a_hip_graph():

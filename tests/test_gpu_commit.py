@@ -73,10 +73,16 @@ def _run_commit(seed, nodes, plens, layers, Hkv, d, head_major=False, max_path=0
     path_h, acc_h = path.cpu().numpy(), acc.cpu().numpy()
     want = owalk.batch_accept_path(np.concatenate(parents), np.concatenate(tokens), oarg.argmax_rows(lg), offs)
     assert [L for _, L, _ in want] == list(acc_h)
-    acc_eff = acc_h if not max_path else np.minimum(acc_h, max_path - 1)
+    # the committed rows follow the oracle's walk, and the device walk must equal it node for node
+    want_path = np.full(N, -1, np.int64)
+    for s, (wp, L, _) in enumerate(want):
+        want_path[offs[s]:offs[s] + L + 1] = wp
+        np.testing.assert_array_equal(path_h[offs[s]:offs[s] + L + 1], wp, err_msg=f"path of sequence {s}")
+    want_acc = np.array([L for _, L, _ in want])
+    acc_eff = want_acc if not max_path else np.minimum(want_acc, max_path - 1)
     for l in range(layers):
         wk, wv = ocommit.commit_kv(host_kc[l], host_vc[l], host_f64(kt[l]).astype(np.float32),
-                                   host_f64(vt[l]).astype(np.float32), path_h, acc_eff, offs, plens, starts)
+                                   host_f64(vt[l]).astype(np.float32), want_path, acc_eff, offs, plens, starts)
         np.testing.assert_array_equal(_bits(kc[l]), _bits(dev_bf16(wk)), err_msg=f"K layer {l}")
         np.testing.assert_array_equal(_bits(vc[l]), _bits(dev_bf16(wv)), err_msg=f"V layer {l}")
     return acc_h

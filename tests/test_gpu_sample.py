@@ -103,8 +103,8 @@ def test_sample_full_size_round():
     check_samples(out.cpu().numpy(), x.cpu().numpy(), 1.0, 0xDEADBEEF12345, 3)
 
 
-def test_sample_full_size_batch_sampled_rows():
-    """2048 rows x 151936 (ragged and long-context batches); 64 sampled rows checked."""
+def test_sample_full_size_batch_all_rows():
+    """2048 rows x 151936 (ragged and long-context batches), every row against the oracle."""
     import torch
 
     require_gpu()
@@ -112,8 +112,7 @@ def test_sample_full_size_batch_sampled_rows():
     print("sample 2048 x 151936", flush=True)
     out = dt.dt_sample_rows(x, 1.0, 77, 1 << 40)
     torch.cuda.synchronize()
-    rows = np.sort(grng.stream(29, "pick").choice(2048, size=64, replace=False))
-    check_samples(out.cpu().numpy()[rows], x.cpu().numpy()[rows], 1.0, 77, 1 << 40, row_ids=rows)
+    check_samples(out.cpu().numpy(), x.cpu().numpy(), 1.0, 77, 1 << 40)
 
 
 @pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
