@@ -7,6 +7,7 @@ in libdtree (host C++ for the tree builder, HIP kernels for the rest).
 
     dt_build_tree       best-first (DDTree) draft-tree construction, host
     dt_tree_attention   ancestor-only tree attention over a KV-cached prefix
+    dt_tree_attention_noalloc  the same without a workspace (a static device buffer)
     dt_argmax_rows      per-node greedy prediction (row arg-max, lowest index on ties)
     dt_sample_rows      per-node target sample at temperature T > 0 (Gumbel-max, Philox4x32-10)
     dt_accept_path      longest accepted root-to-leaf path and bonus token
@@ -25,7 +26,7 @@ from ._lib import dt_attn_desc  # noqa: F401
 
 __all__ = [
     "DtError", "dt_status_string", "dt_abi_version", "dt_build_tree", "dt_validate_tree",
-    "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention",
+    "AttnLayout", "dt_tree_attention_workspace_size", "dt_tree_attention", "dt_tree_attention_noalloc",
     "dt_argmax_rows_workspace_size", "dt_argmax_rows", "dt_sample_rows_workspace_size", "dt_sample_rows",
     "dt_accept_path", "dt_commit_kv", "CommitArgs", "dt_topk_rows_workspace_size", "dt_topk_rows",
     "dt_expand_depth", "dt_prune_topb", "library_path",
@@ -202,15 +203,9 @@ def dt_tree_attention_workspace_size(q, k_tree, k_prefix, layout, scale=None, sp
     return n.value
 
 
-def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, scale=None, split_keys=0,
-                      out=None, workspace=None, stream=None):
-    """Ancestor-only tree attention (GPU).
-
-    q [N, Hq, d], k_tree/v_tree [N, Hkv, d], k_prefix/v_prefix [rows, Hkv, d]
-    (any row/head strides, d contiguous; may be None when every prefix is
-    empty), parent int32 [N] tree-local, all torch CUDA tensors (bf16 for the
-    operands). Returns out [N, Hq, d] bf16.
-    """
+def _check_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out):
+    """Dtypes, devices, shapes and extents of dt_tree_attention's tensors
+    (out may be None); returns the device."""
     import torch
 
     bf = torch.bfloat16
@@ -236,18 +231,34 @@ def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, sca
         ends = layout.prefix_row_start + layout.prefix_lens.astype(np.int64)
         if len(ends) and int(ends.max()) > k_prefix.shape[0]:
             raise ValueError(f"a prefix ends at row {int(ends.max())}, the cache has {k_prefix.shape[0]} rows")
+        if k_prefix.stride() != v_prefix.stride():
+            raise ValueError("k_prefix and v_prefix must share strides")
     elif (layout.prefix_lens > 0).any():
         raise ValueError("non-empty prefixes need k_prefix and v_prefix")
-    if k_prefix is not None and (k_prefix.stride() != v_prefix.stride()):
-        raise ValueError("k_prefix and v_prefix must share strides")
     if k_tree.stride() != v_tree.stride():
         raise ValueError("k_tree and v_tree must share strides")
+    if out is not None:
+        _req(out, "out", bf, dev)
+        if tuple(out.shape) != tuple(q.shape) or out.stride(2) != 1 or (Hq > 1 and out.stride(1) != d):
+            raise ValueError("out: [N, Hq, d] like q, with contiguous heads")
+    return dev
+
+
+def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, scale=None, split_keys=0,
+                      out=None, workspace=None, stream=None):
+    """Ancestor-only tree attention (GPU).
+
+    q [N, Hq, d], k_tree/v_tree [N, Hkv, d], k_prefix/v_prefix [rows, Hkv, d]
+    (any row/head strides, d contiguous; may be None when every prefix is
+    empty), parent int32 [N] tree-local, all torch CUDA tensors (bf16 for the
+    operands). Returns out [N, Hq, d] bf16.
+    """
+    import torch
+
+    dev = _check_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out)
     desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
     if out is None:
-        out = torch.empty(q.shape, dtype=bf, device=dev)
-    _req(out, "out", bf, dev)
-    if tuple(out.shape) != tuple(q.shape) or out.stride(2) != 1 or (Hq > 1 and out.stride(1) != d):
-        raise ValueError("out: [N, Hq, d] like q, with contiguous heads")
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     _req_workspace(workspace, "workspace", dev)
     desc.out_row_stride = _row_stride(out, q.shape[1] * q.shape[2])
     lib = _lib.load()
@@ -255,7 +266,7 @@ def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, sca
     _check(lib.dt_tree_attention_workspace_size(ctypes.byref(desc), ctypes.byref(need)),
            "dt_tree_attention_workspace_size")
     if need.value and workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.dt_tree_attention(ctypes.byref(desc), q.data_ptr(), k_tree.data_ptr(), v_tree.data_ptr(),
@@ -263,6 +274,27 @@ def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, sca
                                v_prefix.data_ptr() if v_prefix is not None else None,
                                parent.data_ptr(), out.data_ptr(), ws_ptr, ws_len, _stream(stream))
     _check(st, "dt_tree_attention")
+    return out
+
+
+def dt_tree_attention_noalloc(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out, scale=None,
+                              split_keys=0, stream=None):
+    """dt_tree_attention without a workspace, for callers that cannot allocate
+    (HIP graph capture, serving loops): the library keeps the split partials in
+    a static device buffer of DT_NOALLOC_SCRATCH_BYTES per GPU. ``out`` is the
+    caller's (this wrapper allocates nothing either). Calls that overlap on one
+    GPU share that buffer and must be serialised by the caller."""
+    if out is None:
+        raise ValueError("dt_tree_attention_noalloc needs the caller's out tensor")
+    _check_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out)
+    desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
+    desc.out_row_stride = _row_stride(out, q.shape[1] * q.shape[2])
+    st = _lib.load().dt_tree_attention_noalloc(ctypes.byref(desc), q.data_ptr(), k_tree.data_ptr(),
+                                               v_tree.data_ptr(),
+                                               k_prefix.data_ptr() if k_prefix is not None else None,
+                                               v_prefix.data_ptr() if v_prefix is not None else None,
+                                               parent.data_ptr(), out.data_ptr(), _stream(stream))
+    _check(st, "dt_tree_attention_noalloc")
     return out
 
 

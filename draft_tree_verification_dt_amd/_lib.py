@@ -77,6 +77,7 @@ SIGNATURES = {
     "dt_validate_tree": (ctypes.c_int, [P_i32, c_i32]),
     "dt_tree_attention_workspace_size": (ctypes.c_int, [ctypes.POINTER(dt_attn_desc), ctypes.POINTER(c_size)]),
     "dt_tree_attention": (ctypes.c_int, [ctypes.POINTER(dt_attn_desc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_size, c_p]),
+    "dt_tree_attention_noalloc": (ctypes.c_int, [ctypes.POINTER(dt_attn_desc), c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "dt_argmax_rows_workspace_size": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_size)]),
     "dt_argmax_rows": (ctypes.c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_size, c_p]),
     "dt_sample_rows_workspace_size": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(c_size)]),

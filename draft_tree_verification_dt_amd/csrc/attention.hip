@@ -50,7 +50,7 @@
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
-#include <vector>
+#include <mutex>
 
 #include "internal.h"
 
@@ -910,14 +910,21 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
 
 // ---------------------------------------------------------------- host side
 
+// The call-wide choices; each launch (a group of at most kMaxSeqs sequences)
+// is derived from them when it is enqueued, so planning touches no heap.
 struct Plan {
-  int wm = 8;                        // row groups per workgroup (64, 128 or 256 rows)
-  std::vector<AttnParams> launches;  // one per group of <= kMaxSeqs sequences
-  std::vector<int> grid;             // workgroups per launch
-  std::vector<int> comb_grid;        // combine blocks per launch (0 = none)
-  std::vector<int> comb_groups;      // chunk groups per combine row (1 or 4)
-  std::vector<size_t> lds;           // dynamic LDS bytes per launch
+  int wm = 8;            // row groups per workgroup (64, 128 or 256 rows)
+  int64_t chunk = 0;     // keys per split
+  size_t part_rows = 0;  // split-partial rows over the whole call
   size_t ws_bytes = 0;
+};
+
+struct Launch {
+  AttnParams a;
+  int grid = 0;         // workgroups
+  int comb_grid = 0;    // combine blocks (0 = none)
+  int comb_groups = 1;  // chunk groups per combine row (1 or 4)
+  size_t lds = 0;       // dynamic LDS bytes
 };
 
 int check_desc(const dt_attn_desc* d) {
@@ -1041,6 +1048,57 @@ bool lds_fits(int D, int wm, int max_n, int g) {
   return static_lds_for(D, wm) + dynamic_lds(max_n, g, wm) <= (size_t)kLdsBytes;
 }
 
+// The launch of sequences [s0, s0 + kMaxSeqs) under a call-wide plan (wm and
+// chunk chosen). *part_rows carries the split-partial rows of the earlier
+// launches in and this launch's end out.
+void plan_launch(const dt_attn_desc* d, const Plan& plan, int s0, size_t* part_rows, Launch* L) {
+  const int g = d->num_q_heads / d->num_kv_heads;
+  const int rm = kWaveRows * plan.wm;
+  AttnParams& a = L->a;
+  std::memset(&a, 0, sizeof(a));
+  a.nseq = std::min(kMaxSeqs, d->num_seqs - s0);
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.g = g;
+  a.chunk = (int32_t)plan.chunk;
+  a.scale_log2 = d->softmax_scale * kLog2e;
+  int items = 0, comb = 0, launch_max_n = 1, max_splits = 1;
+  for (int i = 0; i < a.nseq; ++i) {
+    const int s = s0 + i;
+    SeqGeom& sg = a.seq[i];
+    sg.node_off = d->node_offsets[s];
+    sg.n = d->node_offsets[s + 1] - d->node_offsets[s];
+    sg.P = d->prefix_lens[s];
+    sg.prefix_row0 = d->prefix_row_start[s];
+    sg.row_tiles = (int32_t)ceil_div((int64_t)sg.n * g, rm);
+    sg.splits = (int32_t)std::max<int64_t>(1, ceil_div((int64_t)sg.P + sg.n, plan.chunk));
+    sg.item_start = items;
+    items += sg.row_tiles * sg.splits * d->num_kv_heads;
+    if (sg.splits > 1) {
+      sg.part_base = (int32_t)*part_rows;
+      *part_rows += (size_t)sg.splits * sg.n * d->num_q_heads;
+      sg.comb_start = comb;
+      comb += sg.n * d->num_q_heads;
+    } else {
+      sg.part_base = -1;
+      sg.comb_start = -1;
+    }
+    launch_max_n = std::max(launch_max_n, sg.n);
+    max_splits = std::max(max_splits, sg.splits);
+  }
+  a.total_items = items;
+  a.per_xcd = (int32_t)ceil_div(items, kXcds);
+  a.max_n = launch_max_n;
+  a.mask_words = (launch_max_n + 31) / 32 + 2;
+  a.mask_rows = (rm - 1) / g + 2;
+  a.comb_rows = comb;
+  L->grid = a.per_xcd * kXcds;
+  // many chunks per row: four threads share each (row, slice), more threads carry the loads
+  L->comb_groups = max_splits > 8 ? 4 : 1;
+  L->comb_grid = comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8 * L->comb_groups)) : 0;
+  L->lds = dynamic_lds(launch_max_n, g, plan.wm);
+}
+
 int make_plan(const dt_attn_desc* d, Plan* plan) {
   int st = check_desc(d);
   if (st != DT_OK) return st;
@@ -1075,57 +1133,15 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   const int rm = kWaveRows * wm;
   int64_t chunk = ragged && wm == 8 ? choose_chunk_ragged(d, g, rm, cus) : choose_chunk(d, g, rm, cus);
   if (chunk > (int64_t)1 << 30) chunk = (int64_t)1 << 30;
+  plan->chunk = chunk;
 
   size_t part_rows = 0;
+  Launch L;
   for (int s0 = 0; s0 < d->num_seqs; s0 += kMaxSeqs) {
-    AttnParams a;
-    std::memset(&a, 0, sizeof(a));
-    a.nseq = std::min(kMaxSeqs, d->num_seqs - s0);
-    a.Hq = d->num_q_heads;
-    a.Hkv = d->num_kv_heads;
-    a.g = g;
-    a.chunk = (int32_t)chunk;
-    a.scale_log2 = d->softmax_scale * kLog2e;
-    int items = 0, comb = 0, launch_max_n = 1;
-    for (int i = 0; i < a.nseq; ++i) {
-      const int s = s0 + i;
-      SeqGeom& sg = a.seq[i];
-      sg.node_off = d->node_offsets[s];
-      sg.n = d->node_offsets[s + 1] - d->node_offsets[s];
-      sg.P = d->prefix_lens[s];
-      sg.prefix_row0 = d->prefix_row_start[s];
-      sg.row_tiles = (int32_t)ceil_div((int64_t)sg.n * g, rm);
-      sg.splits = (int32_t)std::max<int64_t>(1, ceil_div((int64_t)sg.P + sg.n, chunk));
-      sg.item_start = items;
-      items += sg.row_tiles * sg.splits * d->num_kv_heads;
-      if (sg.splits > 1) {
-        sg.part_base = (int32_t)part_rows;
-        part_rows += (size_t)sg.splits * sg.n * d->num_q_heads;
-        sg.comb_start = comb;
-        comb += sg.n * d->num_q_heads;
-      } else {
-        sg.part_base = -1;
-        sg.comb_start = -1;
-      }
-      launch_max_n = std::max(launch_max_n, sg.n);
-    }
+    plan_launch(d, *plan, s0, &part_rows, &L);
     if (part_rows > (size_t)INT32_MAX) return DT_ERR_UNSUPPORTED;
-    a.total_items = items;
-    a.per_xcd = (int32_t)ceil_div(items, kXcds);
-    a.max_n = launch_max_n;
-    a.mask_words = (launch_max_n + 31) / 32 + 2;
-    a.mask_rows = (rm - 1) / g + 2;
-    a.comb_rows = comb;
-    plan->launches.push_back(a);
-    plan->grid.push_back(a.per_xcd * kXcds);
-    // many chunks per row: four threads share each (row, slice), more threads carry the loads
-    int max_splits = 1;
-    for (int i = 0; i < a.nseq; ++i) max_splits = std::max(max_splits, a.seq[i].splits);
-    const int cg = max_splits > 8 ? 4 : 1;
-    plan->comb_groups.push_back(cg);
-    plan->comb_grid.push_back(comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8 * cg)) : 0);
-    plan->lds.push_back(dynamic_lds(launch_max_n, g, wm));
   }
+  plan->part_rows = part_rows;
   plan->ws_bytes = part_rows ? round_up(part_rows * (size_t)d->head_dim * sizeof(_Float16), 256) +
                                    round_up(part_rows * sizeof(float4), 256)
                              : 0;
@@ -1154,45 +1170,29 @@ extern "C" int dt_tree_attention_workspace_size(const dt_attn_desc* desc, size_t
   return DT_OK;
 }
 
-extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
-                                 const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace dt;
-  if (!q || !k_tree || !v_tree || !parent || !out) return DT_ERR_NULL;
-  Plan plan;
-  int st = make_plan(desc, &plan);
-  if (st != DT_OK) return st;
-  bool any_prefix = false;
-  for (int s = 0; s < desc->num_seqs; ++s) any_prefix |= desc->prefix_lens[s] > 0;
-  if (any_prefix && (!k_prefix || !v_prefix)) return DT_ERR_NULL;
-  for (const void* ptr : {q, k_tree, v_tree, (const void*)out})
-    if (!aligned(ptr, 16)) return DT_ERR_SHAPE;
-  if (any_prefix && (!aligned(k_prefix, 16) || !aligned(v_prefix, 16))) return DT_ERR_SHAPE;
-  if (!aligned(parent, 4)) return DT_ERR_SHAPE;
-  if (plan.ws_bytes) {
-    if (!workspace || workspace_bytes < plan.ws_bytes) return DT_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return DT_ERR_WORKSPACE;
-  }
+namespace dt {
+namespace {
 
+// Enqueue a planned call (arguments checked by the caller).
+int run_attention(const dt_attn_desc* desc, const Plan& plan, const void* q, const void* k_tree, const void* v_tree,
+                  const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out, void* workspace,
+                  void* stream) {
   const int64_t D = desc->head_dim;
   const int64_t qrs = desc->q_row_stride ? desc->q_row_stride : desc->num_q_heads * D;
   const int64_t ors = desc->out_row_stride ? desc->out_row_stride : desc->num_q_heads * D;
   const int64_t trs = desc->tree_row_stride ? desc->tree_row_stride : desc->num_kv_heads * D;
-  size_t part_rows_bytes = 0;
-  for (auto& a : plan.launches)
-    for (int i = 0; i < a.nseq; ++i)
-      if (a.seq[i].splits > 1)
-        part_rows_bytes = std::max(part_rows_bytes,
-                                   (size_t)(a.seq[i].part_base + (size_t)a.seq[i].splits * a.seq[i].n * a.Hq));
   _Float16* part_o = static_cast<_Float16*>(workspace);
   float4* part_ml = plan.ws_bytes
                         ? reinterpret_cast<float4*>(static_cast<char*>(workspace) +
-                                                    round_up(part_rows_bytes * D * sizeof(_Float16), 256))
+                                                    round_up(plan.part_rows * D * sizeof(_Float16), 256))
                         : nullptr;
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);
-  for (size_t li = 0; li < plan.launches.size(); ++li) {
-    AttnParams a = plan.launches[li];
+  size_t part_rows = 0;
+  Launch L;
+  for (int s0 = 0; s0 < desc->num_seqs; s0 += kMaxSeqs) {
+    plan_launch(desc, plan, s0, &part_rows, &L);
+    AttnParams& a = L.a;
     a.q = static_cast<const bf16_bits*>(q);
     a.kt = static_cast<const bf16_bits*>(k_tree);
     a.vt = static_cast<const bf16_bits*>(v_tree);
@@ -1209,24 +1209,133 @@ extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const 
     a.p_hs = desc->prefix_head_stride;
     if (a.total_items == 0) continue;
     if (D == 128) {
-      launch_fwd<128>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
-      if (plan.comb_grid[li]) {
-        if (plan.comb_groups[li] > 1)
-          hipLaunchKernelGGL((tree_attn_combine<128, 4>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      launch_fwd<128>(plan.wm, L.grid, L.lds, st_, a);
+      if (L.comb_grid) {
+        if (L.comb_groups > 1)
+          hipLaunchKernelGGL((tree_attn_combine<128, 4>), dim3(L.comb_grid), dim3(256), 0, st_, a);
         else
-          hipLaunchKernelGGL((tree_attn_combine<128, 1>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+          hipLaunchKernelGGL((tree_attn_combine<128, 1>), dim3(L.comb_grid), dim3(256), 0, st_, a);
       }
     } else {
-      launch_fwd<64>(plan.wm, plan.grid[li], plan.lds[li], st_, a);
-      if (plan.comb_grid[li]) {
-        if (plan.comb_groups[li] > 1)
-          hipLaunchKernelGGL((tree_attn_combine<64, 4>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+      launch_fwd<64>(plan.wm, L.grid, L.lds, st_, a);
+      if (L.comb_grid) {
+        if (L.comb_groups > 1)
+          hipLaunchKernelGGL((tree_attn_combine<64, 4>), dim3(L.comb_grid), dim3(256), 0, st_, a);
         else
-          hipLaunchKernelGGL((tree_attn_combine<64, 1>), dim3(plan.comb_grid[li]), dim3(256), 0, st_, a);
+          hipLaunchKernelGGL((tree_attn_combine<64, 1>), dim3(L.comb_grid), dim3(256), 0, st_, a);
       }
     }
-    st = launch_status();
+    const int st = launch_status();
     if (st != DT_OK) return st;
   }
   return DT_OK;
+}
+
+// Checks of the buffers shared by both entry points.
+int check_buffers(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
+                  const void* k_prefix, const void* v_prefix, const int32_t* parent, const void* out) {
+  if (!q || !k_tree || !v_tree || !parent || !out) return DT_ERR_NULL;
+  bool any_prefix = false;
+  for (int s = 0; s < desc->num_seqs; ++s) any_prefix |= desc->prefix_lens[s] > 0;
+  if (any_prefix && (!k_prefix || !v_prefix)) return DT_ERR_NULL;
+  for (const void* ptr : {q, k_tree, v_tree, out})
+    if (!aligned(ptr, 16)) return DT_ERR_SHAPE;
+  if (any_prefix && (!aligned(k_prefix, 16) || !aligned(v_prefix, 16))) return DT_ERR_SHAPE;
+  if (!aligned(parent, 4)) return DT_ERR_SHAPE;
+  return DT_OK;
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_tree_attention(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
+                                 const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dt;
+  if (!q || !k_tree || !v_tree || !parent || !out) return DT_ERR_NULL;
+  Plan plan;
+  int st = make_plan(desc, &plan);
+  if (st != DT_OK) return st;
+  st = check_buffers(desc, q, k_tree, v_tree, k_prefix, v_prefix, parent, out);
+  if (st != DT_OK) return st;
+  if (plan.ws_bytes) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return DT_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DT_ERR_WORKSPACE;
+  }
+  return run_attention(desc, plan, q, k_tree, v_tree, k_prefix, v_prefix, parent, out, workspace, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+//
+// dt_tree_attention_noalloc keeps the split partials in this array instead of
+// a caller workspace. Its host-side name is not a device address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is ever passed to
+// kernels. The kernels write every partial before reading it, so the array
+// needs no clearing between calls; calls that overlap on one GPU (other
+// streams, other threads) share it and race.
+static __device__ __align__(256) unsigned char scratch[DT_NOALLOC_SCRATCH_BYTES];
+
+namespace dt {
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+
+int scratch_address(void** ptr) {
+  int dev = 0;
+  DT_TRY_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices) return DT_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return DT_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return DT_OK;
+}
+
+// The default plan, or, when its partials exceed the scratch array, the same
+// call with key chunks doubled until they fit (fewer splits; none at all at
+// worst). A caller-forced chunk is kept, and one too large is an error.
+int plan_within_scratch(const dt_attn_desc* desc, Plan* plan) {
+  int st = make_plan(desc, plan);
+  if (st != DT_OK) return st;
+  if (plan->ws_bytes <= (size_t)DT_NOALLOC_SCRATCH_BYTES) return DT_OK;
+  if (desc->split_keys) return DT_ERR_WORKSPACE;
+  dt_attn_desc d2 = *desc;
+  int64_t chunk = plan->chunk;
+  while (plan->ws_bytes > (size_t)DT_NOALLOC_SCRATCH_BYTES) {
+    chunk *= 2;
+    if (chunk > ((int64_t)1 << 30)) return DT_ERR_WORKSPACE;
+    d2.split_keys = (int32_t)chunk;
+    *plan = Plan();
+    st = make_plan(&d2, plan);
+    if (st != DT_OK) return st;
+  }
+  return DT_OK;
+}
+
+}  // namespace
+}  // namespace dt
+
+extern "C" int dt_tree_attention_noalloc(const dt_attn_desc* desc, const void* q, const void* k_tree,
+                                         const void* v_tree, const void* k_prefix, const void* v_prefix,
+                                         const int32_t* parent, void* out, void* stream) {
+  using namespace dt;
+  if (!q || !k_tree || !v_tree || !parent || !out) return DT_ERR_NULL;
+  Plan plan;
+  int st = plan_within_scratch(desc, &plan);
+  if (st != DT_OK) return st;
+  st = check_buffers(desc, q, k_tree, v_tree, k_prefix, v_prefix, parent, out);
+  if (st != DT_OK) return st;
+  void* ws = nullptr;
+  if (plan.ws_bytes) {
+    st = scratch_address(&ws);
+    if (st != DT_OK) return st;
+  }
+  return run_attention(desc, plan, q, k_tree, v_tree, k_prefix, v_prefix, parent, out, ws, stream);
 }

@@ -15,6 +15,7 @@
  * This library provides that path:
  *   dt_build_tree       host: best-first (DDTree) tree construction
  *   dt_tree_attention   GPU:  ancestor-only tree attention over a KV-cached prefix
+ *   dt_tree_attention_noalloc  the same without a workspace (a static device buffer)
  *   dt_argmax_rows      GPU:  per-node greedy prediction (row arg-max)
  *   dt_sample_rows      GPU:  per-node target sample at temperature T > 0 (Gumbel-max)
  *   dt_accept_path      GPU:  longest accepted path and bonus token
@@ -29,7 +30,9 @@
  *  - Ownership: the caller owns every buffer, host and device. The library
  *    allocates no device memory (scratch comes from a caller-provided
  *    workspace), uses host memory only for temporaries freed before the call
- *    returns, and keeps no pointer after a call returns.
+ *    returns, and keeps no pointer after a call returns. The one exception is
+ *    dt_tree_attention_noalloc, whose scratch is a static device buffer of
+ *    fixed size that the library holds per GPU (see there).
  *  - Device work is enqueued on the caller's HIP stream, passed as `void*`
  *    (a hipStream_t; NULL means the default stream). Outputs are valid once
  *    the stream reaches that point. No call synchronises the stream.
@@ -41,7 +44,9 @@
  *  - DT_ERR_HIP reports a failed HIP runtime call (e.g. a launch error); an
  *    asynchronous device fault surfaces at the caller's next synchronisation.
  *  - The library keeps no mutable global state (device properties are cached
- *    once per device), so calls from several host threads are safe.
+ *    once per device), so calls from several host threads are safe, except
+ *    overlapping dt_tree_attention_noalloc calls on one GPU (they share its
+ *    static buffer).
  *
  * Tree representation (all calls): a tree of n nodes is an int32 array
  * parent[n] with parent[0] == -1 (node 0 is the root: the last committed
@@ -196,6 +201,32 @@ int dt_tree_attention_workspace_size(const dt_attn_desc* desc, size_t* bytes);
 int dt_tree_attention(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device buffer behind dt_tree_attention_noalloc (per GPU). */
+#define DT_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * dt_tree_attention_noalloc -- dt_tree_attention for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same operation, arguments and errors as
+ * dt_tree_attention, without a workspace: the split partials live in a static
+ * device buffer of DT_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * every GPU it runs on until the process ends. The call allocates nothing.
+ *   - When the partials of the default plan would exceed the buffer, the keys
+ *     are processed in larger chunks (fewer splits, possibly none), so every
+ *     valid description runs; results then equal dt_tree_attention's within
+ *     rounding rather than bit for bit.
+ *   - A caller-forced desc->split_keys whose partials exceed the buffer is
+ *     rejected with DT_ERR_WORKSPACE.
+ *   - The buffer keeps the last call's contents. Calls on one stream are
+ *     ordered; calls that overlap on one GPU (other streams or threads) share
+ *     the buffer and race, so the caller serializes them.
+ * Errors: as dt_tree_attention (DT_ERR_WORKSPACE as above; DT_ERR_HIP also
+ * when the buffer's device address cannot be obtained).
+ */
+int dt_tree_attention_noalloc(const dt_attn_desc* desc, const void* q, const void* k_tree, const void* v_tree,
+                              const void* k_prefix, const void* v_prefix, const int32_t* parent, void* out,
+                              void* stream);
 
 /*
  * dt_argmax_rows_workspace_size -- bytes of device workspace dt_argmax_rows
