@@ -4,14 +4,15 @@
 // node for exact target-sample matching at T > 0 (same passage, the DFlash
 // rule; Experimental Setup > Evaluation Details, T = 1).
 //
-// Pure streaming work, bound by HBM bandwidth. Each row is cut into chunks so
-// that the launch has enough workgroups whatever the row count (a 16-node
-// chain has 16 rows of 152K entries; a 2048-node batch has 2048). A workgroup
-// scans its chunk with 16-byte loads, four in flight per thread, keeping the
-// first (lowest-index) maximum per thread; waves reduce with cross-lane
-// shuffles and the four waves through LDS. With one chunk per row the result
-// is written directly; otherwise per-chunk (value, index) pairs go to the
-// workspace and a second kernel merges them. Ties go to the lowest index.
+// Pure streaming work, bound by HBM bandwidth. With at least one row per CU
+// every row is one workgroup; fewer rows are cut into chunks so that the
+// launch has enough workgroups (a 16-node chain has 16 rows of 152K entries; a
+// 2048-node batch has 2048). A workgroup scans its chunk with 16-byte loads,
+// several in flight per thread, keeping the first (lowest-index) maximum per
+// thread; waves reduce with cross-lane shuffles and the waves through LDS.
+// With one chunk per row the result is written directly; otherwise per-chunk
+// (value, index) pairs go to the workspace and a second kernel merges them.
+// Ties go to the lowest index.
 //
 // Sampling (Gumbel-max): argmax_j (l_j / T - ln(-ln U_j)) is an exact draw from
 // softmax(l / T). The uniforms come from Philox4x32-10 (Salmon et al., "Parallel
@@ -21,10 +22,12 @@
 // covers the four entries of a 16-byte load. The kernel compares, in fp32,
 //   s_j = l_j * (log2(e) / T) - log2(-log2 U_j),
 // which is the natural-log score times log2(e) minus a constant, so it ranks
-// the vocabulary exactly as the definition does (up to fp32 rounding). Two of
-// the counter words and the key are uniform across a workgroup, so the first
-// rounds partly run on the scalar unit. Ten rounds of two 32x32->64-bit
-// multiplies per four entries make this variant ALU-bound rather than HBM-bound.
+// the vocabulary exactly as the definition does (up to fp32 rounding). Three of
+// the four counter words (all but the block index) and the key are uniform
+// across a workgroup, so much of the first three rounds is computed once per
+// thread (see RowPhilox). The 32x32->64-bit
+// multiplies (sixteen lane-varying ones per four entries) put this variant's
+// ALU time close to its HBM time.
 
 #include <hip/hip_runtime.h>
 
@@ -52,17 +55,20 @@ struct Gumbel {
   uint32_t o0, o1; // counter words 2 and 3: offset low and high words
 };
 
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;  // round multipliers
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;  // key increments
+
 // Philox4x32-10 of counter (c0, c1, c2, c3) and key (k0, k1), in place.
 __device__ inline void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
                                      uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r > 0) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
     }
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
     // three-input XOR in one VALU op (truth table 0x96)
     const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
     const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
@@ -77,6 +83,70 @@ __device__ inline void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, u
 __device__ inline void gumbel_block(const Gumbel& g, uint32_t row, uint32_t j, uint32_t w[4]) {
   uint32_t c0 = row, c1 = j, c2 = g.o0, c3 = g.o1;
   philox4x32_10(c0, c1, c2, c3, g.k0, g.k1);
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+}
+
+// The same generator for the blocks of one row, restructured: in counter
+// (row, j, o0, o1) only word 1, the block index j, differs between the row's
+// blocks, so most of the first three rounds is the same for all of them. With
+// c0 = j ^ a after round 1 (a, and the other three words, uniform), round 2
+// multiplies one lane-varying word (the other product is uniform) and round 3
+// likewise; the uniform words are computed once per thread (row_philox) and
+// rounds 4-10 run as usual. Sixteen lane-varying products per block instead of
+// twenty; the output words are identical.
+struct RowPhilox {
+  uint32_t a;   // round 1: c0 = j ^ a
+  uint32_t d1;  // round 2: c2 = hi(M0 c0) ^ d1
+  uint32_t jx;  // round 3: c0 = hi(M1 c2) ^ jx
+  uint32_t h;   // round 3: c2 = c3 ^ h
+  uint32_t i;   // round 3: c3 = i
+  uint32_t k0, k1;
+};
+
+__device__ inline RowPhilox row_philox(const Gumbel& g, uint32_t row) {
+  RowPhilox r;
+  const uint64_t p0 = (uint64_t)kPhiloxM0 * row, p1 = (uint64_t)kPhiloxM1 * g.o0;  // round 1
+  r.a = (uint32_t)(p1 >> 32) ^ g.k0;
+  const uint32_t b = (uint32_t)p1, c = (uint32_t)(p0 >> 32) ^ g.o1 ^ g.k1, d = (uint32_t)p0;
+  const uint64_t q1 = (uint64_t)kPhiloxM1 * c;  // round 2, uniform half
+  const uint32_t e = (uint32_t)(q1 >> 32) ^ b ^ (g.k0 + kPhiloxW0), f = (uint32_t)q1;
+  r.d1 = d ^ (g.k1 + kPhiloxW1);
+  r.jx = f ^ (g.k0 + 2 * kPhiloxW0);
+  const uint64_t q0 = (uint64_t)kPhiloxM0 * e;  // round 3, uniform half
+  r.h = (uint32_t)(q0 >> 32) ^ (g.k1 + 2 * kPhiloxW1);
+  r.i = (uint32_t)q0;
+  r.k0 = g.k0;
+  r.k1 = g.k1;
+  return r;
+}
+
+// The four Philox words of block j of the row that rp describes.
+__device__ inline void gumbel_block_row(const RowPhilox& rp, uint32_t j, uint32_t w[4]) {
+  const uint64_t p0 = (uint64_t)kPhiloxM0 * (j ^ rp.a);  // round 2
+  uint32_t c2 = (uint32_t)(p0 >> 32) ^ rp.d1, c3 = (uint32_t)p0;
+  const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;  // round 3
+  uint32_t c0 = (uint32_t)(p1 >> 32) ^ rp.jx, c1 = (uint32_t)p1;
+  c2 = c3 ^ rp.h;
+  c3 = rp.i;
+  uint32_t k0 = rp.k0 + 3 * kPhiloxW0, k1 = rp.k1 + 3 * kPhiloxW1;
+#pragma unroll
+  for (int r = 3; r < 10; ++r) {
+    if (r > 3) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint64_t q0 = (uint64_t)kPhiloxM0 * c0;
+    const uint64_t q1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(q1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(q0 >> 32), c3, k1, 0x96);
+    c1 = (uint32_t)q1;
+    c3 = (uint32_t)q0;
+    c0 = n0;
+    c2 = n2;
+  }
   w[0] = c0;
   w[1] = c1;
   w[2] = c2;
@@ -148,13 +218,13 @@ __device__ inline float entry_value(float l, int64_t t, uint32_t row, const Gumb
 }
 
 // Gumbel scores of the four entries of vocabulary block j.
-__device__ inline f32x4 gumbel4(f32x4 v, uint32_t row, uint32_t j, const Gumbel& g) {
+__device__ inline f32x4 gumbel4(f32x4 v, const RowPhilox& rp, uint32_t j, float c) {
   uint32_t w[4];
-  gumbel_block(g, row, j, w);
-  v.x = gumbel_score(v.x, w[0], g.c);
-  v.y = gumbel_score(v.y, w[1], g.c);
-  v.z = gumbel_score(v.z, w[2], g.c);
-  v.w = gumbel_score(v.w, w[3], g.c);
+  gumbel_block_row(rp, j, w);
+  v.x = gumbel_score(v.x, w[0], c);
+  v.y = gumbel_score(v.y, w[1], c);
+  v.z = gumbel_score(v.z, w[2], c);
+  v.w = gumbel_score(v.w, w[3], c);
   return v;
 }
 
@@ -172,27 +242,66 @@ __global__ __launch_bounds__(THREADS) void argmax_chunks(const float* __restrict
   float bv = -INFINITY;
   int bi = INT_MAX;
   if (VEC) {
+    const RowPhilox rp = SAMPLE ? row_philox(g, (uint32_t)row) : RowPhilox{};
     const int64_t beg4 = beg >> 2, end4 = end >> 2;  // full float4s; beg is a multiple of 4
     const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
     int64_t j = beg4 + threadIdx.x;
-    for (; j + (UNROLL - 1) * THREADS < end4; j += UNROLL * THREADS) {
-      f32x4 v[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(x4 + j + u * THREADS);
+    constexpr int64_t kGroup = (int64_t)UNROLL * THREADS;  // entries (float4s) of one group of loads
+    auto scan_group = [&](f32x4* v, int64_t jj) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int base = (int)((j + u * THREADS) << 2);
-        if (SAMPLE) v[u] = gumbel4(v[u], (uint32_t)row, (uint32_t)(j + u * THREADS), g);
+        const int base = (int)((jj + u * THREADS) << 2);
+        if (SAMPLE) v[u] = gumbel4(v[u], rp, (uint32_t)(jj + u * THREADS), g.c);
         TAKE_IF_LARGER(v[u].x, base);
         TAKE_IF_LARGER(v[u].y, base + 1);
         TAKE_IF_LARGER(v[u].z, base + 2);
         TAKE_IF_LARGER(v[u].w, base + 3);
       }
+    };
+    if (!SAMPLE) {
+      // Greedy: UNROLL loads per thread, then their compares (measured faster
+      // here than keeping the next group in flight during the compares).
+      for (; j + (UNROLL - 1) * THREADS < end4; j += kGroup) {
+        f32x4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(x4 + j + u * THREADS);
+        scan_group(v, j);
+      }
+    } else {
+      // Sampling: the Philox arithmetic is long, so the next group's loads
+      // are in flight while this one is scored (double-buffered). Pairs of
+      // groups per iteration, with no exit between a group's loads and its
+      // compares, so that neither the scheduler (the barrier) nor the
+      // optimiser moves the loads below the previous group's work; the last
+      // prefetch of an even count re-reads the current group (in range, unused).
+      const int64_t groups =
+          end4 > j + (UNROLL - 1) * THREADS ? (end4 - j - (UNROLL - 1) * THREADS - 1) / kGroup + 1 : 0;
+      auto load_group = [&](f32x4* v, int64_t jj) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(x4 + jj + u * THREADS);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (groups > 0) {
+        f32x4 va[UNROLL], vb[UNROLL];
+        load_group(va, j);
+        int64_t gq = 0;
+        for (; gq + 2 <= groups; gq += 2) {
+          load_group(vb, j + kGroup);
+          scan_group(va, j);
+          load_group(va, gq + 2 < groups ? j + 2 * kGroup : j);
+          scan_group(vb, j + kGroup);
+          j += 2 * kGroup;
+        }
+        if (gq < groups) {
+          scan_group(va, j);
+          j += kGroup;
+        }
+      }
     }
     for (; j < end4; j += THREADS) {
       f32x4 v = __builtin_nontemporal_load(x4 + j);
       const int base = (int)(j << 2);
-      if (SAMPLE) v = gumbel4(v, (uint32_t)row, (uint32_t)j, g);
+      if (SAMPLE) v = gumbel4(v, rp, (uint32_t)j, g.c);
       TAKE_IF_LARGER(v.x, base);
       TAKE_IF_LARGER(v.y, base + 1);
       TAKE_IF_LARGER(v.z, base + 2);
@@ -238,24 +347,28 @@ __global__ __launch_bounds__(256) void argmax_merge(int64_t rows, int64_t vocab,
   if (lane == 0) out_idx[row] = (bi >= 0 && bi < vocab) ? bi : 0;
 }
 
-// Greedy scans of at least one row per CU take one 512-thread workgroup per row
-// (8 loads in flight per thread, 64 KB per workgroup: with a workgroup on every
-// CU that is about what HBM needs in flight), so no merge kernel runs. The
-// sampling scan keeps more, smaller workgroups per CU, which its Philox
-// arithmetic needs to overlap with the loads. Fewer rows are cut into chunks of
-// 256-thread workgroups and merged.
+// Scans of at least one row per CU take one workgroup per row, so no merge
+// kernel runs. Greedy: 512 threads (8 loads in flight per thread, 64 KB per
+// workgroup: with a workgroup on every CU that is about what HBM needs in
+// flight). Sampling: 1024 threads with 4 loads each below eight rows per CU
+// (four waves per SIMD, so the Philox arithmetic of some waves overlaps the
+// loads of others), and 256-thread workgroups from eight rows per CU on,
+// where several workgroups share each CU. Fewer rows than CUs are cut into
+// chunks of 256-thread workgroups and merged.
 constexpr int kWideThreads = 512;
 constexpr int kWideUnroll = 8;
+constexpr int kSampleWideThreads = 1024;
+constexpr int kSampleWideUnroll = 4;
 
-int plan_chunks(int64_t rows, int64_t vocab, int cus, bool sample, int64_t* chunk_len, int* chunks) {
-  if (!sample && rows >= cus) {
+int plan_chunks(int64_t rows, int64_t vocab, int cus, int64_t* chunk_len, int* chunks) {
+  if (rows >= cus) {
     *chunk_len = vocab;
     *chunks = 1;
     return DT_OK;
   }
   // enough workgroups to cover the CUs several times over, chunks >= 8K entries
   const int64_t target_wg = 8LL * cus;
-  int64_t c = rows >= target_wg ? 1 : ceil_div(target_wg, std::max<int64_t>(rows, 1));
+  int64_t c = ceil_div(target_wg, std::max<int64_t>(rows, 1));
   c = std::min<int64_t>(c, std::max<int64_t>(1, vocab / 8192));
   int64_t len = ceil_div(ceil_div(vocab, c), kChunkQuantum) * kChunkQuantum;
   c = ceil_div(vocab, len);
@@ -271,7 +384,7 @@ int plan_chunks(int64_t rows, int64_t vocab, int cus, bool sample, int64_t* chun
 namespace dt {
 namespace {
 
-int scan_workspace_size(int64_t rows, int64_t vocab, bool sample, size_t* bytes) {
+int scan_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
   if (!bytes) return DT_ERR_NULL;
   if (rows < 0 || vocab < 1 || vocab > INT_MAX) return DT_ERR_SHAPE;
   int cus = 0;
@@ -279,7 +392,7 @@ int scan_workspace_size(int64_t rows, int64_t vocab, bool sample, size_t* bytes)
   if (st != DT_OK) return st;
   int64_t len;
   int chunks;
-  st = plan_chunks(rows, vocab, cus, sample, &len, &chunks);
+  st = plan_chunks(rows, vocab, cus, &len, &chunks);
   if (st != DT_OK) return st;
   *bytes = chunks > 1 ? round_up((size_t)rows * chunks * sizeof(float2), 256) : 0;
   return DT_OK;
@@ -289,7 +402,7 @@ int scan_workspace_size(int64_t rows, int64_t vocab, bool sample, size_t* bytes)
 }  // namespace dt
 
 extern "C" int dt_argmax_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
-  return dt::scan_workspace_size(rows, vocab, false, bytes);
+  return dt::scan_workspace_size(rows, vocab, bytes);
 }
 
 namespace dt {
@@ -302,7 +415,7 @@ int launch_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_st
   if (st != DT_OK) return st;
   int64_t len;
   int chunks;
-  st = plan_chunks(rows, vocab, cus, sample, &len, &chunks);
+  st = plan_chunks(rows, vocab, cus, &len, &chunks);
   if (st != DT_OK) return st;
   float2* part = nullptr;
   if (chunks > 1) {
@@ -314,9 +427,13 @@ int launch_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_st
   const bool vec = aligned(logits, 16) && (row_stride % 4 == 0);
   dim3 grid((unsigned)chunks, (unsigned)rows);
   const bool wide = !sample && rows >= cus;
+  const bool sample_wide = sample && rows >= cus && rows < 8LL * cus;
 #define DT_LAUNCH_SCAN(V, S)                                                                                         \
   do {                                                                                                              \
-    if (wide)                                                                                                       \
+    if (sample_wide)                                                                                                \
+      hipLaunchKernelGGL((argmax_chunks<V, S, kSampleWideThreads, kSampleWideUnroll>), grid, dim3(kSampleWideThreads), \
+                         0, s, logits, vocab, row_stride, len, chunks, out_idx, part, g);                           \
+    else if (wide)                                                                                                  \
       hipLaunchKernelGGL((argmax_chunks<V, S, kWideThreads, kWideUnroll>), grid, dim3(kWideThreads), 0, s, logits,  \
                          vocab, row_stride, len, chunks, out_idx, part, g);                                         \
     else                                                                                                            \
@@ -357,7 +474,7 @@ extern "C" int dt_argmax_rows(const float* logits, int64_t rows, int64_t vocab, 
 }
 
 extern "C" int dt_sample_rows_workspace_size(int64_t rows, int64_t vocab, size_t* bytes) {
-  return dt::scan_workspace_size(rows, vocab, true, bytes);
+  return dt::scan_workspace_size(rows, vocab, bytes);
 }
 
 extern "C" int dt_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride, float temperature,
