@@ -4,17 +4,23 @@
 // Best-First Pruning, eq. 5-6 with Lemma 1).
 //
 // All three are selections "the best m of M candidates" under a total order
-// (value descending, then a candidate index ascending). One block-wide routine
-// does them all: a most-significant-digit radix select (four 8-bit passes with
-// an LDS histogram) finds the m-th best value, a second radix select over the
-// candidate indices of the elements equal to it resolves ties by lowest index,
-// and the selected elements are gathered and, where the caller needs them in
-// order, sorted with a bitonic network in LDS. No pass depends on the data's
-// distribution, and exact ties are handled, so the result is the definition's.
+// (value descending, then a candidate index ascending). Two block-wide routines
+// do them. select_ordered first filters: a threshold that provably admits the
+// best m (from the waves' sorted per-thread bests, or a caller's hint) leaves a
+// few candidates, each ranked against the others, which yields them in order.
+// When too many pass, and in the pruning step, a most-significant-digit radix
+// select (four 8-bit passes with an LDS histogram) finds the m-th best value, a
+// second radix select over the candidate indices of the elements equal to it
+// resolves ties by lowest index, and the selected elements are gathered and
+// sorted with a bitonic network in LDS. Exact ties are handled either way, so
+// the result is the definition's.
 //
 //   topk_chunks + topk_merge   C_d = TopK(L_d, K) over the vocabulary, with the
 //                              log-softmax value of every kept token (the row's
-//                              log-sum-exp is merged from per-chunk (max, sum))
+//                              log-sum-exp is merged from per-chunk (max, sum));
+//                              each chunk's K best are written in order, so the
+//                              merge takes its filter threshold from the lists'
+//                              heads
 //   expand_kernel              one depth: scores (s_parent + log q~) + beta of all
 //                              W_prev x K children, the best W kept in order
 //   prune_kernel               the best B supertree nodes by (score, depth,
@@ -26,6 +32,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -35,7 +42,8 @@ namespace {
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxCand = 16384;  // candidates one block selects from (64 per thread)
 constexpr int kSelPerThread = kSelMaxCand / kSelThreads;
-constexpr int kTopkChunk = 4096;    // vocabulary entries per chunk workgroup (16 per thread)
+constexpr int kTopkChunkSmall = 4096;   // vocabulary entries per chunk workgroup (16 per thread)
+constexpr int kTopkChunkLarge = 10240;  // ... from 16 rows on (40 per thread: about one workgroup per CU)
 constexpr int kMaxSortedK = 1024;   // largest selection that is returned in order
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -52,11 +60,52 @@ __device__ inline float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Maximum and sum over a wave: DPP moves within each 16-lane row (quad
+// swaps, then the row's halves, then its two halves of eight), then the four
+// rows' values read as scalars.
+template <int CTRL>
+__device__ inline float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));   // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_move<0x4E>(v));   // quad_perm 2,3,0,1
+  v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ inline float wave_sum(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  auto mv = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  v = mv(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mv(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mv(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = mv(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return mv(mv((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+            mv((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[256];  // digit histogram; the threads' best keys in select_ordered
   uint32_t red[kSelThreads / 64];
   uint32_t bin, remaining, in_bin, total;
   uint32_t count;
+  uint32_t thr;  // select_ordered's candidate threshold
 };
 
 // Keys are never 0 for a candidate (float_key of a finite value, or the bitwise
@@ -250,7 +299,155 @@ struct SelLds {
   int32_t ord[kMaxSortedK];
   uint32_t tk[kMaxSortedK];
   int32_t ti[kMaxSortedK];
+  uint2 cand[kSelThreads];  // select_ordered's candidates (key, index) and payloads
+  int32_t cp0[kSelThreads];
+  int32_t cp1[kSelThreads];
 };
+
+// The value held by lane (this lane ^ J) of the wave, J a power of two below
+// 64: DPP quad permutations for 1 and 2, the swizzle crossbar for 4 to 16,
+// a permute for 32.
+template <int J>
+__device__ inline uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (J << 10));
+  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), (int)v);
+}
+
+// Bitonic sort of the wave's 64 values (one per lane), largest in lane 0.
+__device__ inline uint32_t wave_sort_desc(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+  auto step = [&](auto JJ, int k) __attribute__((always_inline)) {
+    constexpr int J = decltype(JJ)::value;
+    const uint32_t o = lane_xor<J>(v);
+    // within a block of k lanes sorted descending when (lane & k) == 0: the
+    // lower lane of a pair keeps the larger value
+    const bool lower = (lane & J) == 0;
+    const bool desc = (lane & k) == 0;
+    v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  using I32 = std::integral_constant<int, 32>;
+  step(I1{}, 2);
+  step(I2{}, 4), step(I1{}, 4);
+  step(I4{}, 8), step(I2{}, 8), step(I1{}, 8);
+  step(I8{}, 16), step(I4{}, 16), step(I2{}, 16), step(I1{}, 16);
+  step(I16{}, 32), step(I8{}, 32), step(I4{}, 32), step(I2{}, 32), step(I1{}, 32);
+  step(I32{}, 64), step(I16{}, 64), step(I8{}, 64), step(I4{}, 64), step(I2{}, 64), step(I1{}, 64);
+  return v;
+}
+
+// (key, index) as one 64-bit word that orders as (key desc, index asc) does.
+__device__ inline uint64_t rank_word(uint32_t key, int32_t idx) { return ((uint64_t)key << 32) | (uint32_t)~idx; }
+
+// Select the best m candidates (non-zero keys) by (key desc, idx asc), in
+// order: on return L.key/idx/p0/p1[r] hold the r-th best for r < the returned
+// count (min(m, candidates), uniform across the block) and L.ord[r] = r.
+//
+// Most selections have few contenders near the top, so a filter comes first.
+// Every wave sorts its 64 threads' own best keys; with q = ceil(m / 4), let t
+// be the smallest of the four waves' q-th largest (t = 1, i.e. every
+// candidate, when a wave has fewer than q non-empty threads). The waves' q best
+// thread keys are 4q >= m distinct candidates with keys >= t, so the m-th best
+// key is >= t and every one of the best m passes the filter key >= t. When at
+// most one candidate per thread passes, each is ranked against all the others
+// (its rank is its position in the order; indices are unique, so ranks are
+// distinct); otherwise the radix select and the sort below run as usual.
+//
+// A caller that knows a valid threshold (one with at least m candidates at
+// or above it) passes it as `hint` (0: none), and the waves' sort is skipped.
+// The ranking splits each candidate's comparisons over 2 or 4 adjacent lanes
+// when there are at most 128 or 64 candidates.
+template <int E, bool PAY>
+__device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E], const int32_t (&p0)[E],
+                              const int32_t (&p1)[E], uint32_t m, SelShared& sh, SelLds& L, uint32_t hint = 0) {
+  if (m == 0) return 0;
+  if (threadIdx.x == 0) sh.count = 0u;
+  uint32_t thr = 1u;
+  if (hint) {
+    thr = hint;
+    __syncthreads();
+  } else if (m <= (uint32_t)kSelThreads) {
+    uint32_t best = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
+    const uint32_t sorted = wave_sort_desc(best);
+    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)((m + 3) / 4 - 1));
+    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tw;
+    __syncthreads();
+    uint32_t t = sh.red[0];
+#pragma unroll
+    for (int w = 1; w < kSelThreads / 64; ++w) t = sh.red[w] < t ? sh.red[w] : t;
+    thr = t ? t : 1u;
+  } else {
+    __syncthreads();
+  }
+  // this thread's candidates: counted first, then one atomic reserves their slots
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += (key[e] != 0u && key[e] >= thr) ? 1u : 0u;
+  if (mine) {
+    uint32_t pos = atomicAdd(&sh.count, mine);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (key[e] != 0u && key[e] >= thr) {
+        if (pos < (uint32_t)kSelThreads) {
+          L.cand[pos] = make_uint2(key[e], (uint32_t)idx[e]);
+          if (PAY) {
+            L.cp0[pos] = p0[e];
+            L.cp1[pos] = p1[e];
+          }
+        }
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = sh.count;
+  if (n > (uint32_t)kSelThreads) {
+    const int got = (int)select_best<E, PAY>(key, idx, p0, p1, m, sh, L.key, L.idx, L.p0, L.p1);
+    order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+    return got;
+  }
+  // lanes per candidate: 4 (n <= 64), 2 (n <= 128) or 1; lane `part` of a
+  // candidate's group compares it with every lpc-th candidate from `part` on
+  const int lpc = n <= 64 ? 4 : (n <= 128 ? 2 : 1);
+  const uint32_t ci = threadIdx.x / lpc, part = threadIdx.x % lpc;
+  const uint2 c = L.cand[ci < n ? ci : 0];
+  const uint64_t wc = rank_word(c.x, (int32_t)c.y);
+  uint32_t r = 0;
+  // eight reads in flight per step (the trip count is only known at run time,
+  // so the compiler would otherwise wait for every read in turn)
+  for (uint32_t jb = part; jb < n; jb += 8u * lpc) {
+    uint2 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t j = jb + u * lpc;
+      o[u] = L.cand[j < n ? j : 0u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += (jb + u * lpc < n && rank_word(o[u].x, (int32_t)o[u].y) > wc) ? 1u : 0u;
+  }
+  // the group's partial counts (the lpc lanes of a group are adjacent, within a quad)
+  if (lpc >= 2) r += lane_xor<1>(r);
+  if (lpc >= 4) r += lane_xor<2>(r);
+  if (part == 0 && ci < n && r < m) {
+    L.key[r] = c.x;
+    L.idx[r] = (int32_t)c.y;
+    if (PAY) {
+      L.p0[r] = L.cp0[ci];
+      L.p1[r] = L.cp1[ci];
+    }
+    L.ord[r] = (int32_t)r;
+  }
+  __syncthreads();
+  return (int)(n < m ? n : m);
+}
 
 // ---------------------------------------------------------------- top-K of rows
 
@@ -265,15 +462,17 @@ struct TopkParams {
   float* out_logprob;   // [rows][k]
 };
 
-// grid (chunks, rows): the chunk's best k entries and its (max, sum exp) pair.
-template <bool VEC>
+// grid (chunks, rows): the chunk's best k entries, in order, and its (max, sum
+// exp) pair. A chunk is E entries per thread.
+template <bool VEC, int E>
 __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   __shared__ SelShared sh;
+  __shared__ SelLds L;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   const float* xr = p.x + row * p.stride;
-  const int64_t beg = (int64_t)c * kTopkChunk;
-  constexpr int E = kTopkChunk / kSelThreads;  // 16
+  const int64_t beg = (int64_t)c * (kSelThreads * E);
+  static_assert(E % 4 == 0, "16-byte loads");
   float v[E];
   uint32_t key[E];
   int32_t idx[E];
@@ -302,8 +501,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (valid[e]) m = fmaxf(m, v[e]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = wave_max(m);
   __shared__ float wm[kSelThreads / 64], ws[kSelThreads / 64];
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -312,19 +510,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (valid[e]) s += __expf(v[e] - m);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = valid[e] ? float_key(v[e]) : 0u;
-  __syncthreads();
+  // (select_ordered's first barrier also publishes ws)
+  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L);
   const size_t base = ((size_t)row * p.chunks + c) * p.k;
   if (threadIdx.x == 0) p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, (ws[0] + ws[1]) + (ws[2] + ws[3]));
-  const uint32_t got =
-      select_best<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, p.part_key + base, p.part_idx + base, nullptr, nullptr);
-  for (int j = (int)got + threadIdx.x; j < p.k; j += kSelThreads) {  // a short last chunk: pad
-    p.part_key[base + j] = 0u;
-    p.part_idx[base + j] = -1;
+  // the chunk's best k in order; a short last chunk pads with empty slots
+  for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
+    const bool ok = r < got;
+    p.part_key[base + r] = ok ? L.key[L.ord[r]] : 0u;
+    p.part_idx[base + r] = ok ? L.idx[L.ord[r]] : -1;
   }
 }
 
@@ -338,36 +536,52 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   const int64_t row = blockIdx.x;
   const int M = p.chunks * p.k;
   const size_t base = (size_t)row * M;
-  // log-sum-exp of the row from the chunk pairs
-  float m = -INFINITY;
-  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) m = fmaxf(m, p.part_stat[(size_t)row * p.chunks + c].x);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float s = 0.f;
-  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) {
-    const float2 st = p.part_stat[(size_t)row * p.chunks + c];
-    s += st.y * __expf(st.x - m);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
+  // the chunks' candidates (keys and indices requested together; padding of a
+  // short chunk has key 0, an empty slot) and their (max, sum) pairs
+  // Each thread takes a contiguous run of slots (the chunks' lists are sorted,
+  // so a run mixes ranks, which keeps select_ordered's filter tight).
+  const int per = (M + kSelThreads - 1) / kSelThreads;  // <= E
   uint32_t key[E];
   int32_t idx[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = threadIdx.x + kSelThreads * e;
-    const bool in = j < M;
+    const int j = threadIdx.x * per + e;
+    const bool in = e < per && j < M;
+    key[e] = in ? p.part_key[base + j] : 0u;
     idx[e] = in ? p.part_idx[base + j] : -1;
-    key[e] = (in && idx[e] >= 0) ? p.part_key[base + j] : 0u;  // padding of a short chunk: empty
   }
-  const int got = (int)select_best<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L.key, L.idx, nullptr, nullptr);
-  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  const float2* ps = p.part_stat + (size_t)row * p.chunks;
+  const float2 st = threadIdx.x < p.chunks ? ps[threadIdx.x] : make_float2(-INFINITY, 0.f);
+  // log-sum-exp of the row from the chunk pairs
+  float m = st.x;
+  for (int c = threadIdx.x + kSelThreads; c < p.chunks; c += kSelThreads) m = fmaxf(m, ps[c].x);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float s = threadIdx.x < p.chunks ? st.y * __expf(st.x - m) : 0.f;
+  for (int c = threadIdx.x + kSelThreads; c < p.chunks; c += kSelThreads) s += ps[c].y * __expf(ps[c].x - m);
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
+  // Each chunk's list is sorted, so with r0 = ceil(k / chunks) the first r0
+  // entries of every list are >= chunks * r0 >= k distinct candidates, all at
+  // or above the smallest of the lists' r0-th entries: a valid threshold for
+  // select_ordered (0, no hint, if a short list has an empty slot there).
+  const int r0 = (p.k + p.chunks - 1) / p.chunks;
+  uint32_t tmin = 0xFFFFFFFFu;
+  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) {
+    const uint32_t kc = p.part_key[base + (size_t)c * p.k + r0 - 1];
+    tmin = kc < tmin ? kc : tmin;
+  }
+  tmin = wave_min_u32(tmin);
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tmin;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) tmin = sh.red[w] < tmin ? sh.red[w] : tmin;
+  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L, tmin == 0xFFFFFFFFu ? 0u : tmin);
   for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
     const bool ok = r < got;
     const int j = ok ? L.ord[r] : 0;
@@ -403,24 +617,27 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
   const float* lq = p.child_logq + s * p.lq_stride;
   const int32_t* ct = p.cand_token + s * p.ct_stride;
   const int M = p.w_prev * p.k;
+  // a contiguous run of children per thread (each parent's candidates come
+  // sorted, so a run mixes ranks, which keeps select_ordered's filter tight)
+  const int per = (M + kSelThreads - 1) / kSelThreads;  // <= E
   uint32_t key[E];
   int32_t idx[E], tok[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = threadIdx.x + kSelThreads * e;
+    const int j = threadIdx.x * per + e;
+    const bool in = e < per && j < M;
     float sc = -INFINITY;
     tok[e] = -1;
-    if (j < M) {
+    if (in) {
       const int par = j / p.k;
       const float a = ps[par] + lq[j];  // Algorithm 1, line 8, in this order
       sc = a + p.beta;
       tok[e] = ct[j - par * p.k];
     }
-    key[e] = (j < M && isfinite(sc)) ? float_key(sc) : 0u;
-    idx[e] = j;
+    key[e] = (in && isfinite(sc)) ? float_key(sc) : 0u;
+    idx[e] = in ? j : -1;
   }
-  const int got = (int)select_best<E, true>(key, idx, tok, tok, (uint32_t)p.w, sh, L.key, L.idx, L.p0, L.p1);
-  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  const int got = select_ordered<E, true>(key, idx, tok, tok, (uint32_t)p.w, sh, L);
   const int64_t o = s * p.out_stride;
   for (int r = threadIdx.x; r < p.w; r += kSelThreads) {
     const bool ok = r < got;
@@ -476,6 +693,8 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   }
   for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
   if (threadIdx.x == 0) bad = 0;
+  // (the radix select: here the budget is a third of the candidates, too many
+  // for select_ordered's filter to pay)
   const int got = (int)select_best<E, true>(key, idx, tok, par, (uint32_t)p.budget, sh, L.key, L.idx, L.p0, L.p1);
   order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
   for (int r = threadIdx.x; r < got; r += kSelThreads) newpos[L.idx[L.ord[r]]] = (int16_t)(r + 1);
@@ -538,11 +757,15 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   }
 }
 
+// Chunk size: 10240 entries from 16 rows on (about one workgroup per CU for
+// a 16-row, 152K-entry table, and fewer lists to merge), 4096 below.
+int topk_chunk_len(int64_t rows) { return rows >= 16 ? kTopkChunkLarge : kTopkChunkSmall; }
+
 int topk_plan(int64_t rows, int64_t vocab, int32_t k, int* chunks) {
   if (rows < 0 || vocab < 1 || vocab > INT_MAX) return DT_ERR_SHAPE;
   if (k < 1 || k > vocab) return DT_ERR_SHAPE;
   if (k > kMaxSortedK || rows > 65535) return DT_ERR_UNSUPPORTED;
-  const int64_t c = ceil_div(vocab, kTopkChunk);
+  const int64_t c = ceil_div(vocab, topk_chunk_len(rows));
   if (c * k > kSelMaxCand || c > 65535) return DT_ERR_UNSUPPORTED;
   *chunks = (int)c;
   return DT_OK;
@@ -593,10 +816,15 @@ extern "C" int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, in
   p.out_logprob = out_logprob;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = aligned(logits, 16) && row_stride % 4 == 0;
-  if (vec)
-    hipLaunchKernelGGL(topk_chunks<true>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(topk_chunks<false>, dim3((unsigned)chunks, (unsigned)rows), dim3(kSelThreads), 0, s, p);
+  const dim3 cgrid((unsigned)chunks, (unsigned)rows);
+  constexpr int kEL = kTopkChunkLarge / kSelThreads, kES = kTopkChunkSmall / kSelThreads;
+  if (topk_chunk_len(rows) == kTopkChunkLarge) {
+    if (vec) hipLaunchKernelGGL((topk_chunks<true, kEL>), cgrid, dim3(kSelThreads), 0, s, p);
+    else hipLaunchKernelGGL((topk_chunks<false, kEL>), cgrid, dim3(kSelThreads), 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((topk_chunks<true, kES>), cgrid, dim3(kSelThreads), 0, s, p);
+    else hipLaunchKernelGGL((topk_chunks<false, kES>), cgrid, dim3(kSelThreads), 0, s, p);
+  }
   const int64_t M = (int64_t)chunks * k;
   if (M <= 4 * kSelThreads)
     hipLaunchKernelGGL(topk_merge<4>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
