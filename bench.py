@@ -398,9 +398,33 @@ def time_small_tree(rnd, reps=40, n=16):
             raise dt.DtError(st, "dt_tree_attention")
 
     ms = time_on_stream(rnd, call, reps)
+    ms_b2b = time_back_to_back(rnd, call, reps)
     nbytes = 2 * P * Hkv * d * 2 + n * (2 * Hq * d * 2 + 2 * Hkv * d * 2 + 4)
     flops = 4.0 * d * Hq * (n * P + n * (n + 1) // 2)
-    return ms, nbytes, flops
+    return ms, ms_b2b, nbytes, flops
+
+
+def time_stream_floor(rnd, nbytes, tables=10, reps=40):
+    """The practical floor of one kernel that streams `nbytes` from HBM: the
+    library's arg-max scan over a [256, nbytes / 1024] fp32 table (one
+    workgroup per row, nothing but loads and compares), rotating through
+    `tables` tables (more bytes than the 256 MB last-level cache holds), timed
+    as a single call and back to back like the small-tree call."""
+    torch = rnd.torch
+    cols = nbytes // (256 * 4) // 4 * 4
+    tabs = [torch.randn((256, cols), device=rnd.dev, dtype=torch.float32) for _ in range(tables)]
+    out = torch.empty(256, dtype=torch.int32, device=rnd.dev)
+
+    def call(i):
+        lg = tabs[i % tables]
+        st = rnd.lib.dt_argmax_rows(lg.data_ptr(), 256, cols, cols, out.data_ptr(), None, 0, rnd.stream)
+        if st != 0:
+            raise rnd.dt.DtError(st, "dt_argmax_rows")
+
+    single = time_on_stream(rnd, call, reps)
+    b2b = time_back_to_back(rnd, call, reps)
+    del tabs
+    return single, b2b, 256 * cols * 4
 
 
 OTHER_WORKLOADS = (("b128", 40), ("ragged", 6), ("long", 3))  # (workload, rotating layer caches)
@@ -759,13 +783,21 @@ def main():
         others = {name: time_attention_workload(rnd, name, layers) for name, layers in OTHER_WORKLOADS}
     small = None
     if w.num_seqs == 1:
-        ch_ms, ch_bytes, ch_flops = time_small_tree(rnd)
+        ch_ms, ch_b2b_ms, ch_bytes, ch_flops = time_small_tree(rnd)
+        sf_ms, sf_b2b_ms, sf_bytes = time_stream_floor(rnd, ch_bytes)
         ch_gbs = ch_bytes / (ch_ms / 1e3) / 1e9
         small = {"workload": f"16-node chain (parent[i] = i - 1) over the same {w.prefix_lens[0]}-token prefix",
                  "bound": "hbm", "us": round(ch_ms * 1e3, 2), "achieved": round(ch_gbs, 1), "peak": PEAK_HBM_GBS,
                  "unit": "GB/s", "frac": round(ch_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": ch_bytes,
                  "TFLOP/s": round(ch_flops / (ch_ms / 1e3) / 1e12, 1),
-                 "tree_over_chain_time": round(att_mean_ms / ch_ms, 2)}
+                 "tree_over_chain_time": round(att_mean_ms / ch_ms, 2),
+                 "timing": "single call between an event pair (us); consecutive calls (us_back_to_back)",
+                 "us_back_to_back": round(ch_b2b_ms * 1e3, 2),
+                 "stream_floor": {"kernel": "dt_argmax_rows over a [256, n] fp32 table of the same bytes: one kernel, "
+                                            "one workgroup per row, loads and compares only",
+                                  "bytes": sf_bytes, "us": round(sf_ms * 1e3, 2),
+                                  "us_back_to_back": round(sf_b2b_ms * 1e3, 2),
+                                  "GB/s_back_to_back": round(sf_bytes / (sf_b2b_ms / 1e3) / 1e9, 1)}}
     achieved = flops_layer / (att_mean_ms / 1e3) / 1e12
     argmax_bytes = w.total_nodes * w.vocab * 4 + w.total_nodes * 4
     traffic = recorded_traffic(w)
