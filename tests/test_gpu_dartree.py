@@ -72,6 +72,25 @@ def test_topk_ties_and_special_values():
     _check_topk(x, 1000)
 
 
+def test_topk_ties_in_large_chunks():
+    """From 16 rows on the chunks hold 10240 entries and the merge takes its
+    threshold from the chunks' ordered lists: heavy ties there (few distinct
+    levels, a tie across a 10240-entry chunk boundary, equal chunk maxima) go
+    through the filtered selection's fallback and the merge's threshold on
+    equal keys."""
+    require_gpu()
+    r = grng.stream(6, "topk-ties-large")
+    x = r.standard_normal((20, 40000)).astype(np.float32)
+    x[0, :] = np.round(x[0] * 2) / 2               # few distinct levels
+    x[1, :] = 2.0                                  # all equal
+    x[2, 10238:10242] = 9.0                        # a tie across a chunk boundary
+    x[3, ::10240] = 7.0                            # the same maximum in every chunk
+    x[4, :] = np.round(x[4])                       # fewer levels still
+    print("topk ties, 20 rows", flush=True)
+    _check_topk(x, 64)
+    _check_topk(x, 200)
+
+
 def _random_expand_case(r, S, w_prev, k, ties):
     ps = np.sort(-np.abs(r.standard_normal((S, w_prev))).astype(F32) * F32(3), axis=1)[:, ::-1].copy()
     ps[:, 0] = F32(0.0) if w_prev == 1 else ps[:, 0]
