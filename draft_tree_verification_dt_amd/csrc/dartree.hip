@@ -299,7 +299,7 @@ struct SelLds {
   int32_t ord[kMaxSortedK];
   uint32_t tk[kMaxSortedK];
   int32_t ti[kMaxSortedK];
-  uint2 cand[kSelThreads];  // select_ordered's candidates (key, index) and payloads
+  uint64_t cand[kSelThreads];  // select_ordered's candidates (rank words; 0: empty) and payloads
   int32_t cp0[kSelThreads];
   int32_t cp1[kSelThreads];
 };
@@ -342,8 +342,55 @@ __device__ inline uint32_t wave_sort_desc(uint32_t v) {
   return v;
 }
 
-// (key, index) as one 64-bit word that orders as (key desc, index asc) does.
+// Inclusive prefix sum over the wave's 64 lanes: shifts by 1, 2, 4 and 8
+// within each 16-lane row (lanes shifted in from outside the row add 0), then
+// the row totals carried forward by the row broadcasts of lanes 15 and 31.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_add(uint32_t v) {
+  return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ inline uint32_t wave_incl_sum(uint32_t v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// (key, index) as one 64-bit word that orders as (key desc, index asc) does;
+// 0 is below every candidate's word (keys of candidates are non-zero).
 __device__ inline uint64_t rank_word(uint32_t key, int32_t idx) { return ((uint64_t)key << 32) | (uint32_t)~idx; }
+__device__ inline uint32_t word_key(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ inline int32_t word_idx(uint64_t w) { return (int32_t)~(uint32_t)w; }
+
+// Ranks of the first n words of w (n <= 256; the slots from n up to the next
+// multiple of 8 * lpc hold 0): lane `part` of the lpc adjacent lanes given
+// word `ci` counts the words above it among every lpc-th slot from `part` on,
+// eight reads in flight per step, and the group's counts are summed. lpc is 4
+// (n <= 64), 2 (n <= 128) or 1; ci = threadIdx.x / lpc may be >= n (its word
+// is then a padding 0 or past the words; the caller ignores it).
+__device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& mine, uint32_t& ci, uint32_t& part) {
+  const uint32_t lpc = n <= 64 ? 4u : (n <= 128 ? 2u : 1u);
+  ci = threadIdx.x / lpc;
+  part = threadIdx.x % lpc;
+  mine = w[ci];
+  const uint32_t step = 8u * lpc;
+  const uint32_t end = (n + step - 1) / step * step;
+  uint32_t r = 0;
+  for (uint32_t jb = part; jb < end; jb += step) {
+    uint64_t o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = w[jb + u * lpc];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += o[u] > mine ? 1u : 0u;
+  }
+  // the lpc lanes of a group are adjacent, within a quad
+  if (lpc >= 2) r += lane_xor<1>(r);
+  if (lpc >= 4) r += lane_xor<2>(r);
+  return r;
+}
 
 // Select the best m candidates (non-zero keys) by (key desc, idx asc), in
 // order: on return L.key/idx/p0/p1[r] hold the r-th best for r < the returned
@@ -355,19 +402,22 @@ __device__ inline uint64_t rank_word(uint32_t key, int32_t idx) { return ((uint6
 // candidate, when a wave has fewer than q non-empty threads). The waves' q best
 // thread keys are 4q >= m distinct candidates with keys >= t, so the m-th best
 // key is >= t and every one of the best m passes the filter key >= t. When at
-// most one candidate per thread passes, each is ranked against all the others
-// (its rank is its position in the order; indices are unique, so ranks are
-// distinct); otherwise the radix select and the sort below run as usual.
+// most 256 candidates pass, each is ranked against all the others (its rank is
+// its position in the order; indices are unique, so ranks are distinct);
+// otherwise the radix select and the sort below run as usual.
 //
 // A caller that knows a valid threshold (one with at least m candidates at
 // or above it) passes it as `hint` (0: none), and the waves' sort is skipped.
-// The ranking splits each candidate's comparisons over 2 or 4 adjacent lanes
-// when there are at most 128 or 64 candidates.
+// Passing candidates get their slots from a prefix sum over each wave and one
+// LDS atomic per wave; the slots past the last candidate stay 0, so the
+// ranking (rank_in_lds) reads whole groups of eight with no bounds checks.
 template <int E, bool PAY>
 __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E], const int32_t (&p0)[E],
                               const int32_t (&p1)[E], uint32_t m, SelShared& sh, SelLds& L, uint32_t hint = 0) {
   if (m == 0) return 0;
+  static_assert(E <= 64, "one bit per slot");
   if (threadIdx.x == 0) sh.count = 0u;
+  L.cand[threadIdx.x] = 0ull;  // published by the barrier below, before any slot is written
   uint32_t thr = 1u;
   if (hint) {
     thr = hint;
@@ -387,24 +437,34 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
   } else {
     __syncthreads();
   }
-  // this thread's candidates: counted first, then one atomic reserves their slots
-  uint32_t mine = 0;
+  // this thread's candidates as bits (kept opaque, so that the compiler does
+  // not carry E compare masks in scalar registers to the writes below)
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) mine += (key[e] != 0u && key[e] >= thr) ? 1u : 0u;
-  if (mine) {
-    uint32_t pos = atomicAdd(&sh.count, mine);
+  for (int e = 0; e < E; ++e) {
+    const uint32_t in = key[e] >= thr ? 1u : 0u;  // thr >= 1: no empty slot passes
+    if (e < 32) lo |= in << e;
+    else hi |= in << (e - 32);
+  }
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  const uint32_t mine = __builtin_popcount(lo) + __builtin_popcount(hi);
+  const uint32_t incl = wave_incl_sum(mine);
+  const uint32_t wave_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (wave_total) {  // uniform over the wave
+    uint32_t wbase = 0;
+    if ((threadIdx.x & 63) == 63) wbase = atomicAdd(&sh.count, wave_total);
+    uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + incl - mine;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (key[e] != 0u && key[e] >= thr) {
-        if (pos < (uint32_t)kSelThreads) {
-          L.cand[pos] = make_uint2(key[e], (uint32_t)idx[e]);
-          if (PAY) {
-            L.cp0[pos] = p0[e];
-            L.cp1[pos] = p1[e];
-          }
+      const uint32_t in = ((e < 32 ? lo : hi) >> (e & 31)) & 1u;
+      if (in && pos < (uint32_t)kSelThreads) {
+        L.cand[pos] = rank_word(key[e], idx[e]);
+        if (PAY) {
+          L.cp0[pos] = p0[e];
+          L.cp1[pos] = p1[e];
         }
-        ++pos;
       }
+      pos += in;
     }
   }
   __syncthreads();
@@ -414,31 +474,12 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
     order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
     return got;
   }
-  // lanes per candidate: 4 (n <= 64), 2 (n <= 128) or 1; lane `part` of a
-  // candidate's group compares it with every lpc-th candidate from `part` on
-  const int lpc = n <= 64 ? 4 : (n <= 128 ? 2 : 1);
-  const uint32_t ci = threadIdx.x / lpc, part = threadIdx.x % lpc;
-  const uint2 c = L.cand[ci < n ? ci : 0];
-  const uint64_t wc = rank_word(c.x, (int32_t)c.y);
-  uint32_t r = 0;
-  // eight reads in flight per step (the trip count is only known at run time,
-  // so the compiler would otherwise wait for every read in turn)
-  for (uint32_t jb = part; jb < n; jb += 8u * lpc) {
-    uint2 o[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t j = jb + u * lpc;
-      o[u] = L.cand[j < n ? j : 0u];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) r += (jb + u * lpc < n && rank_word(o[u].x, (int32_t)o[u].y) > wc) ? 1u : 0u;
-  }
-  // the group's partial counts (the lpc lanes of a group are adjacent, within a quad)
-  if (lpc >= 2) r += lane_xor<1>(r);
-  if (lpc >= 4) r += lane_xor<2>(r);
+  uint64_t wc;
+  uint32_t ci, part;
+  const uint32_t r = rank_in_lds(L.cand, n, wc, ci, part);
   if (part == 0 && ci < n && r < m) {
-    L.key[r] = c.x;
-    L.idx[r] = (int32_t)c.y;
+    L.key[r] = word_key(wc);
+    L.idx[r] = word_idx(wc);
     if (PAY) {
       L.p0[r] = L.cp0[ci];
       L.p1[r] = L.cp1[ci];
@@ -476,12 +517,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   float v[E];
   uint32_t key[E];
   int32_t idx[E];
-  bool valid[E];  // only for the max and sum below; the selection uses key != 0
+  // Entries past the vocabulary (only in a row's last chunk) read as -inf,
+  // which changes neither the maximum nor the sum below, and get key 0 (an
+  // empty slot) at the end; a chunk wholly inside the row has no such checks.
+  const bool full = VEC && beg + (int64_t)kSelThreads * E <= p.vocab;  // uniform
   // entry e of thread t: 4 * (t + 256 * (e / 4)) + e % 4 within the chunk (16-byte loads, coalesced)
 #pragma unroll
   for (int q = 0; q < E / 4; ++q) {
     const int64_t i0 = beg + 4 * ((int64_t)threadIdx.x + kSelThreads * q);
-    if (VEC && i0 + 3 < p.vocab) {
+    if (full || (VEC && i0 + 3 < p.vocab)) {
       const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
       v[4 * q] = t.x;
       v[4 * q + 1] = t.y;
@@ -492,15 +536,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
       for (int j = 0; j < 4; ++j) v[4 * q + j] = i0 + j < p.vocab ? xr[i0 + j] : -INFINITY;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      idx[4 * q + j] = (int32_t)(i0 + j);
-      valid[4 * q + j] = i0 + j < p.vocab;
-    }
+    for (int j = 0; j < 4; ++j) idx[4 * q + j] = (int32_t)(i0 + j);
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (valid[e]) m = fmaxf(m, v[e]);
+  for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
   m = wave_max(m);
   __shared__ float wm[kSelThreads / 64], ws[kSelThreads / 64];
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
@@ -508,12 +548,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (valid[e]) s += __expf(v[e] - m);
+  for (int e = 0; e < E; ++e) s += __expf(v[e] - m);
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = valid[e] ? float_key(v[e]) : 0u;
+  for (int e = 0; e < E; ++e) key[e] = (full || idx[e] < p.vocab) ? float_key(v[e]) : 0u;
   // (select_ordered's first barrier also publishes ws)
   const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L);
   const size_t base = ((size_t)row * p.chunks + c) * p.k;
@@ -567,21 +606,34 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   __syncthreads();
   const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
   // Each chunk's list is sorted, so with r0 = ceil(k / chunks) the first r0
-  // entries of every list are >= chunks * r0 >= k distinct candidates, all at
-  // or above the smallest of the lists' r0-th entries: a valid threshold for
-  // select_ordered (0, no hint, if a short list has an empty slot there).
+  // entries of every list are |S| = chunks * r0 >= k distinct candidates; the
+  // k-th best of S is a valid threshold for select_ordered (at least k
+  // candidates reach it), and a tight one: besides S only list entries past
+  // the r0-th that beat it pass. It is found by ranking S's members against
+  // each other (|S| <= 256); no hint (0) when S is larger or a short list has
+  // an empty slot in it (then no member has rank k - 1 among the non-empty).
   const int r0 = (p.k + p.chunks - 1) / p.chunks;
-  uint32_t tmin = 0xFFFFFFFFu;
-  for (int c = threadIdx.x; c < p.chunks; c += kSelThreads) {
-    const uint32_t kc = p.part_key[base + (size_t)c * p.k + r0 - 1];
-    tmin = kc < tmin ? kc : tmin;
+  const int ns = p.chunks * r0;
+  uint32_t tmin = 0u;
+  if (ns <= kSelThreads) {
+    const int j = threadIdx.x;
+    uint64_t w = 0;
+    if (j < ns) {
+      const size_t slot = base + (size_t)(j / r0) * p.k + (j % r0);
+      const uint32_t sk = p.part_key[slot];
+      w = sk ? rank_word(sk, p.part_idx[slot]) : 0ull;
+    }
+    L.cand[j] = w;  // zero past |S|, as rank_in_lds needs
+    if (j == 0) sh.thr = 0u;
+    __syncthreads();
+    uint64_t ws;
+    uint32_t ci, part;
+    const uint32_t r = rank_in_lds(L.cand, (uint32_t)ns, ws, ci, part);
+    if (part == 0 && ci < (uint32_t)ns && ws != 0ull && r == (uint32_t)p.k - 1) sh.thr = word_key(ws);
+    __syncthreads();  // also: every read of L.cand is done before select_ordered clears it
+    tmin = sh.thr;
   }
-  tmin = wave_min_u32(tmin);
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tmin;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) tmin = sh.red[w] < tmin ? sh.red[w] : tmin;
-  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L, tmin == 0xFFFFFFFFu ? 0u : tmin);
+  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L, tmin);
   for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
     const bool ok = r < got;
     const int j = ok ? L.ord[r] : 0;
