@@ -8,8 +8,8 @@
 // do them. select_ordered first filters: a threshold that provably admits the
 // best m (from the waves' sorted per-thread bests, or a caller's hint) leaves a
 // few candidates, each ranked against the others, which yields them in order.
-// When too many pass, and in the pruning step, a most-significant-digit radix
-// select (four 8-bit passes with an LDS histogram) finds the m-th best value, a
+// When more than 256 pass, a most-significant-digit radix select (four 8-bit
+// passes with an LDS histogram) finds the m-th best value, a
 // second radix select over the candidate indices of the elements equal to it
 // resolves ties by lowest index, and the selected elements are gathered and
 // sorted with a bitonic network in LDS. Exact ties are handled either way, so
@@ -745,10 +745,7 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   }
   for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
   if (threadIdx.x == 0) bad = 0;
-  // (the radix select: here the budget is a third of the candidates, too many
-  // for select_ordered's filter to pay)
-  const int got = (int)select_best<E, true>(key, idx, tok, par, (uint32_t)p.budget, sh, L.key, L.idx, L.p0, L.p1);
-  order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  const int got = select_ordered<E, true>(key, idx, tok, par, (uint32_t)p.budget, sh, L);
   for (int r = threadIdx.x; r < got; r += kSelThreads) newpos[L.idx[L.ord[r]]] = (int16_t)(r + 1);
   __syncthreads();
   // With beta <= 0 and log-probabilities <= 0 a child never precedes its parent
