@@ -39,11 +39,15 @@
 namespace dt {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;    // threads of the expansion workgroup
+constexpr int kPruneThreads = 512;  // threads of the pruning workgroup (its ranking: two lanes per candidate)
+constexpr int kChunkThreads = 512;  // two waves per SIMD while a chunk is selected
+constexpr int kMergeThreads = 512;  // ... and while a row's chunk lists are merged
+constexpr int kSelCand = 256;       // candidates select_ordered ranks (more: the radix select)
 constexpr int kSelMaxCand = 16384;  // candidates one block selects from (64 per thread)
 constexpr int kSelPerThread = kSelMaxCand / kSelThreads;
-constexpr int kTopkChunkSmall = 4096;   // vocabulary entries per chunk workgroup (16 per thread)
-constexpr int kTopkChunkLarge = 10240;  // ... from 16 rows on (40 per thread: about one workgroup per CU)
+constexpr int kTopkChunkSmall = 4096;   // vocabulary entries per chunk workgroup (8 per thread)
+constexpr int kTopkChunkLarge = 10240;  // ... from 16 rows on (20 per thread: about one workgroup per CU)
 constexpr int kMaxSortedK = 1024;   // largest selection that is returned in order
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -102,7 +106,7 @@ __device__ inline uint32_t wave_min_u32(uint32_t v) {
 
 struct SelShared {
   uint32_t hist[256];  // digit histogram; the threads' best keys in select_ordered
-  uint32_t red[kSelThreads / 64];
+  uint32_t red[16];  // one per wave (up to 1024 threads)
   uint32_t bin, remaining, in_bin, total;
   uint32_t count;
   uint32_t thr;  // select_ordered's candidate threshold
@@ -115,10 +119,11 @@ struct SelShared {
 // digit equal `prefix` (mask selects them); then wave 0 finds, counting from the
 // top bin down, the bin holding the `remaining`-th key, and publishes it with
 // the count of keys above it, its own count and the total.
-template <int E>
+template <int E, int NT>
 __device__ void digit_pass(const uint32_t (&key)[E], uint32_t prefix, uint32_t mask, int shift, uint32_t remaining,
                            SelShared& sh) {
-  sh.hist[threadIdx.x] = 0;  // 256 threads, 256 bins
+  static_assert(NT >= 256, "one thread per bin");
+  if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < E; ++e)
@@ -153,11 +158,11 @@ __device__ void digit_pass(const uint32_t (&key)[E], uint32_t prefix, uint32_t m
 
 // The m-th largest key (1 <= m <= number of non-zero keys) and how many keys
 // equal to it belong to the best m (used for index tie-breaks only).
-template <int E>
+template <int E, int NT>
 __device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh, uint32_t& thr, uint32_t& need_eq) {
   uint32_t prefix = 0, mask = 0, remaining = m;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    digit_pass<E>(key, prefix, mask, shift, remaining, sh);
+    digit_pass<E, NT>(key, prefix, mask, shift, remaining, sh);
     prefix |= sh.bin << shift;
     mask |= 0xFFu << shift;
     remaining = sh.remaining;
@@ -176,7 +181,7 @@ __device__ void radix_select(const uint32_t (&key)[E], uint32_t m, SelShared& sh
 // taken whole (its count equals what is still needed) ends the search: every
 // key at or above that bin's lowest value is in. Only when the last digit
 // leaves a tie does a second radix select over the tied indices run.
-template <int E, bool PAY>
+template <int E, bool PAY, int NT>
 __device__ uint32_t select_best(const uint32_t (&key)[E], const int32_t (&idx)[E], const int32_t (&p0)[E],
                                 const int32_t (&p1)[E], uint32_t m, SelShared& sh, uint32_t* out_key, int32_t* out_idx,
                                 int32_t* out_p0, int32_t* out_p1) {
@@ -186,7 +191,7 @@ __device__ uint32_t select_best(const uint32_t (&key)[E], const int32_t (&idx)[E
   bool tie = false;                                     // mode B: key > prefix, or == prefix and idx <= idx_thr
   uint32_t idx_thr = 0xFFFFFFFFu, take = m;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    digit_pass<E>(key, prefix, mask, shift, remaining, sh);
+    digit_pass<E, NT>(key, prefix, mask, shift, remaining, sh);
     const uint32_t total = sh.total, bin = sh.bin, rem = sh.remaining, in_bin = sh.in_bin;
     __syncthreads();
     if (shift == 24 && total <= m) {  // everything is taken
@@ -206,7 +211,7 @@ __device__ uint32_t select_best(const uint32_t (&key)[E], const int32_t (&idx)[E
 #pragma unroll
       for (int e = 0; e < E; ++e) ikey[e] = key[e] == prefix ? ~(uint32_t)idx[e] : 0u;  // largest ~idx first
       uint32_t t2, unused;
-      radix_select<E>(ikey, remaining, sh, t2, unused);
+      radix_select<E, NT>(ikey, remaining, sh, t2, unused);
       idx_thr = ~t2;
     }
   }
@@ -246,9 +251,11 @@ __device__ inline int pow2_at_least(int n) {
 // the r-th best; sk and si are left as they are. Up to 256 entries every thread
 // ranks one entry against all of them (no barriers inside the loop); more are
 // sorted by a bitonic network over copies (tk, ti) that carries the positions.
+template <int NT>
 __device__ void order_selected(const uint32_t* sk, const int32_t* si, int n, int32_t* ord, uint32_t* tk,
                                int32_t* ti) {
-  if (n <= kSelThreads) {
+  static_assert(NT >= 256, "one thread per entry up to 256");
+  if (n <= 256) {
     const int j = threadIdx.x;
     if (j < n) {
       const uint32_t kj = sk[j];
@@ -261,7 +268,7 @@ __device__ void order_selected(const uint32_t* sk, const int32_t* si, int n, int
     return;
   }
   const int np = pow2_at_least(n);  // padding sorts behind every real entry
-  for (int j = threadIdx.x; j < np; j += kSelThreads) {
+  for (int j = threadIdx.x; j < np; j += NT) {
     tk[j] = j < n ? sk[j] : 0u;
     ti[j] = j < n ? si[j] : INT_MAX;
     ord[j] = j;
@@ -269,7 +276,7 @@ __device__ void order_selected(const uint32_t* sk, const int32_t* si, int n, int
   __syncthreads();
   for (int size = 2; size <= np; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < np / 2; i += kSelThreads) {
+      for (int i = threadIdx.x; i < np / 2; i += NT) {
         const int a = 2 * i - (i & (stride - 1));
         const int b = a + stride;
         const bool best_first = (a & size) == 0;
@@ -299,9 +306,9 @@ struct SelLds {
   int32_t ord[kMaxSortedK];
   uint32_t tk[kMaxSortedK];
   int32_t ti[kMaxSortedK];
-  uint64_t cand[kSelThreads];  // select_ordered's candidates (rank words; 0: empty) and payloads
-  int32_t cp0[kSelThreads];
-  int32_t cp1[kSelThreads];
+  uint64_t cand[kSelCand];  // select_ordered's candidates (rank words; 0: empty) and payloads
+  int32_t cp0[kSelCand];
+  int32_t cp1[kSelCand];
 };
 
 // The value held by lane (this lane ^ J) of the wave, J a power of two below
@@ -366,13 +373,16 @@ __device__ inline uint32_t word_key(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ inline int32_t word_idx(uint64_t w) { return (int32_t)~(uint32_t)w; }
 
 // Ranks of the first n words of w (n <= 256; the slots from n up to the next
-// multiple of 8 * lpc hold 0): lane `part` of the lpc adjacent lanes given
-// word `ci` counts the words above it among every lpc-th slot from `part` on,
-// eight reads in flight per step, and the group's counts are summed. lpc is 4
-// (n <= 64), 2 (n <= 128) or 1; ci = threadIdx.x / lpc may be >= n (its word
-// is then a padding 0 or past the words; the caller ignores it).
+// multiple of 8 * lpc hold 0), NT threads: lane `part` of the lpc adjacent
+// lanes given word `ci` counts the words above it among every lpc-th slot from
+// `part` on, eight reads in flight per step, and the group's counts are summed.
+// lpc is NT / 64 (n <= 64), NT / 128 (n <= 128) or NT / 256, at most 16; ci =
+// threadIdx.x / lpc may be >= n (its word is then a padding 0 or past the
+// words; the caller ignores it).
+template <int NT>
 __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& mine, uint32_t& ci, uint32_t& part) {
-  const uint32_t lpc = n <= 64 ? 4u : (n <= 128 ? 2u : 1u);
+  static_assert(NT == 256 || NT == 512 || NT == 1024, "whole groups of lanes per wave");
+  const uint32_t lpc = n <= 64 ? NT / 64 : (n <= 128 ? NT / 128 : NT / 256);
   ci = threadIdx.x / lpc;
   part = threadIdx.x % lpc;
   mine = w[ci];
@@ -386,9 +396,11 @@ __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& 
 #pragma unroll
     for (int u = 0; u < 8; ++u) r += o[u] > mine ? 1u : 0u;
   }
-  // the lpc lanes of a group are adjacent, within a quad
+  // the lpc lanes of a group are adjacent, within sixteen
   if (lpc >= 2) r += lane_xor<1>(r);
   if (lpc >= 4) r += lane_xor<2>(r);
+  if (lpc >= 8) r += lane_xor<4>(r);
+  if (lpc >= 16) r += lane_xor<8>(r);
   return r;
 }
 
@@ -397,11 +409,12 @@ __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& 
 // count (min(m, candidates), uniform across the block) and L.ord[r] = r.
 //
 // Most selections have few contenders near the top, so a filter comes first.
-// Every wave sorts its 64 threads' own best keys; with q = ceil(m / 4), let t
-// be the smallest of the four waves' q-th largest (t = 1, i.e. every
-// candidate, when a wave has fewer than q non-empty threads). The waves' q best
-// thread keys are 4q >= m distinct candidates with keys >= t, so the m-th best
-// key is >= t and every one of the best m passes the filter key >= t. When at
+// With NT threads, i.e. W = NT / 64 waves, every wave sorts its 64 threads' own
+// best keys; with q = ceil(m / W), let t be the smallest q-th largest among the
+// F waves that have q non-empty threads. Their q best thread keys are F q
+// distinct candidates with keys >= t, so when F q >= m the m-th best key is
+// >= t and every one of the best m passes the filter key >= t (otherwise t =
+// 1: every candidate passes). When at
 // most 256 candidates pass, each is ranked against all the others (its rank is
 // its position in the order; indices are unique, so ranks are distinct);
 // otherwise the radix select and the sort below run as usual.
@@ -411,29 +424,35 @@ __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& 
 // Passing candidates get their slots from a prefix sum over each wave and one
 // LDS atomic per wave; the slots past the last candidate stay 0, so the
 // ranking (rank_in_lds) reads whole groups of eight with no bounds checks.
-template <int E, bool PAY>
+template <int E, bool PAY, int NT>
 __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E], const int32_t (&p0)[E],
                               const int32_t (&p1)[E], uint32_t m, SelShared& sh, SelLds& L, uint32_t hint = 0) {
   if (m == 0) return 0;
   static_assert(E <= 64, "one bit per slot");
   if (threadIdx.x == 0) sh.count = 0u;
-  L.cand[threadIdx.x] = 0ull;  // published by the barrier below, before any slot is written
+  if (threadIdx.x < kSelCand) L.cand[threadIdx.x] = 0ull;  // published by the barrier below, before any slot is written
   uint32_t thr = 1u;
   if (hint) {
     thr = hint;
     __syncthreads();
-  } else if (m <= (uint32_t)kSelThreads) {
+  } else if (m <= (uint32_t)kSelCand) {
+    constexpr int kWaves = NT / 64;
+    const uint32_t q = (m + kWaves - 1) / kWaves;
     uint32_t best = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
     const uint32_t sorted = wave_sort_desc(best);
-    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)((m + 3) / 4 - 1));
+    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)(q - 1));  // 0: under q non-empty threads
     if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tw;
     __syncthreads();
-    uint32_t t = sh.red[0];
+    uint32_t t = 0xFFFFFFFFu, full = 0;
 #pragma unroll
-    for (int w = 1; w < kSelThreads / 64; ++w) t = sh.red[w] < t ? sh.red[w] : t;
-    thr = t ? t : 1u;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t tv = sh.red[w];
+      full += tv ? 1u : 0u;
+      t = (tv && tv < t) ? tv : t;
+    }
+    thr = full * q >= m ? t : 1u;
   } else {
     __syncthreads();
   }
@@ -457,7 +476,7 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t in = ((e < 32 ? lo : hi) >> (e & 31)) & 1u;
-      if (in && pos < (uint32_t)kSelThreads) {
+      if (in && pos < (uint32_t)kSelCand) {
         L.cand[pos] = rank_word(key[e], idx[e]);
         if (PAY) {
           L.cp0[pos] = p0[e];
@@ -469,14 +488,14 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
   }
   __syncthreads();
   const uint32_t n = sh.count;
-  if (n > (uint32_t)kSelThreads) {
-    const int got = (int)select_best<E, PAY>(key, idx, p0, p1, m, sh, L.key, L.idx, L.p0, L.p1);
-    order_selected(L.key, L.idx, got, L.ord, L.tk, L.ti);
+  if (n > (uint32_t)kSelCand) {
+    const int got = (int)select_best<E, PAY, NT>(key, idx, p0, p1, m, sh, L.key, L.idx, L.p0, L.p1);
+    order_selected<NT>(L.key, L.idx, got, L.ord, L.tk, L.ti);
     return got;
   }
   uint64_t wc;
   uint32_t ci, part;
-  const uint32_t r = rank_in_lds(L.cand, n, wc, ci, part);
+  const uint32_t r = rank_in_lds<NT>(L.cand, n, wc, ci, part);
   if (part == 0 && ci < n && r < m) {
     L.key[r] = word_key(wc);
     L.idx[r] = word_idx(wc);
@@ -503,16 +522,17 @@ struct TopkParams {
   float* out_logprob;   // [rows][k]
 };
 
-// grid (chunks, rows): the chunk's best k entries, in order, and its (max, sum
-// exp) pair. A chunk is E entries per thread.
+// grid (chunks, rows), kChunkThreads threads: the chunk's best k entries, in
+// order, and its (max, sum exp) pair. A chunk is E entries per thread.
 template <bool VEC, int E>
-__global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
+__global__ __launch_bounds__(kChunkThreads) void topk_chunks(const TopkParams p) {
+  constexpr int NT = kChunkThreads;
   __shared__ SelShared sh;
   __shared__ SelLds L;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   const float* xr = p.x + row * p.stride;
-  const int64_t beg = (int64_t)c * (kSelThreads * E);
+  const int64_t beg = (int64_t)c * (NT * E);
   static_assert(E % 4 == 0, "16-byte loads");
   float v[E];
   uint32_t key[E];
@@ -520,11 +540,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
   // Entries past the vocabulary (only in a row's last chunk) read as -inf,
   // which changes neither the maximum nor the sum below, and get key 0 (an
   // empty slot) at the end; a chunk wholly inside the row has no such checks.
-  const bool full = VEC && beg + (int64_t)kSelThreads * E <= p.vocab;  // uniform
-  // entry e of thread t: 4 * (t + 256 * (e / 4)) + e % 4 within the chunk (16-byte loads, coalesced)
+  const bool full = VEC && beg + (int64_t)NT * E <= p.vocab;  // uniform
+  // entry e of thread t: 4 * (t + NT * (e / 4)) + e % 4 within the chunk (16-byte loads, coalesced)
 #pragma unroll
   for (int q = 0; q < E / 4; ++q) {
-    const int64_t i0 = beg + 4 * ((int64_t)threadIdx.x + kSelThreads * q);
+    const int64_t i0 = beg + 4 * ((int64_t)threadIdx.x + NT * q);
     if (full || (VEC && i0 + 3 < p.vocab)) {
       const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
       v[4 * q] = t.x;
@@ -542,10 +562,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 #pragma unroll
   for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
   m = wave_max(m);
-  __shared__ float wm[kSelThreads / 64], ws[kSelThreads / 64];
+  constexpr int kWaves = NT / 64;
+  __shared__ float wm[kWaves], ws[kWaves];
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  m = wm[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, wm[w]);
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) s += __expf(v[e] - m);
@@ -554,24 +577,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunks(const TopkParams p) {
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = (full || idx[e] < p.vocab) ? float_key(v[e]) : 0u;
   // (select_ordered's first barrier also publishes ws)
-  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L);
+  const int got = select_ordered<E, false, NT>(key, idx, idx, idx, (uint32_t)p.k, sh, L);
   const size_t base = ((size_t)row * p.chunks + c) * p.k;
-  if (threadIdx.x == 0) p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, (ws[0] + ws[1]) + (ws[2] + ws[3]));
+  if (threadIdx.x == 0) {
+    float s_all = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s_all += ws[w];
+    p.part_stat[(size_t)row * p.chunks + c] = make_float2(m, s_all);
+  }
   // the chunk's best k in order; a short last chunk pads with empty slots
-  for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
+  for (int r = threadIdx.x; r < p.k; r += NT) {
     const bool ok = r < got;
     p.part_key[base + r] = ok ? L.key[L.ord[r]] : 0u;
     p.part_idx[base + r] = ok ? L.idx[L.ord[r]] : -1;
   }
 }
 
-// grid (rows): merge the chunks' candidates and statistics; k best in order.
-// E candidate slots per thread (E * 256 >= chunks * k).
+// grid (rows), kMergeThreads threads: merge the chunks' candidates and
+// statistics; k best in order. E candidate slots per thread (E * kMergeThreads
+// >= chunks * k).
 template <int E>
-__global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
+__global__ __launch_bounds__(kMergeThreads) void topk_merge(const TopkParams p) {
+  constexpr int NT = kMergeThreads, kWaves = NT / 64;
   __shared__ SelShared sh;
   __shared__ SelLds L;
-  __shared__ float red[kSelThreads / 64];
+  __shared__ float red[kWaves];
   const int64_t row = blockIdx.x;
   const int M = p.chunks * p.k;
   const size_t base = (size_t)row * M;
@@ -579,7 +609,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   // short chunk has key 0, an empty slot) and their (max, sum) pairs
   // Each thread takes a contiguous run of slots (the chunks' lists are sorted,
   // so a run mixes ranks, which keeps select_ordered's filter tight).
-  const int per = (M + kSelThreads - 1) / kSelThreads;  // <= E
+  const int per = (M + NT - 1) / NT;  // <= E
   uint32_t key[E];
   int32_t idx[E];
 #pragma unroll
@@ -593,18 +623,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   const float2 st = threadIdx.x < p.chunks ? ps[threadIdx.x] : make_float2(-INFINITY, 0.f);
   // log-sum-exp of the row from the chunk pairs
   float m = st.x;
-  for (int c = threadIdx.x + kSelThreads; c < p.chunks; c += kSelThreads) m = fmaxf(m, ps[c].x);
+  for (int c = threadIdx.x + NT; c < p.chunks; c += NT) m = fmaxf(m, ps[c].x);
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
   __syncthreads();
   float s = threadIdx.x < p.chunks ? st.y * __expf(st.x - m) : 0.f;
-  for (int c = threadIdx.x + kSelThreads; c < p.chunks; c += kSelThreads) s += ps[c].y * __expf(ps[c].x - m);
+  for (int c = threadIdx.x + NT; c < p.chunks; c += NT) s += ps[c].y * __expf(ps[c].x - m);
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  const float lse = m + __logf((red[0] + red[1]) + (red[2] + red[3]));
+  float s_all = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s_all += red[w];
+  const float lse = m + __logf(s_all);
   // Each chunk's list is sorted, so with r0 = ceil(k / chunks) the first r0
   // entries of every list are |S| = chunks * r0 >= k distinct candidates; the
   // k-th best of S is a valid threshold for select_ordered (at least k
@@ -615,7 +650,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
   const int r0 = (p.k + p.chunks - 1) / p.chunks;
   const int ns = p.chunks * r0;
   uint32_t tmin = 0u;
-  if (ns <= kSelThreads) {
+  if (ns <= kSelCand) {
     const int j = threadIdx.x;
     uint64_t w = 0;
     if (j < ns) {
@@ -623,18 +658,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge(const TopkParams p) {
       const uint32_t sk = p.part_key[slot];
       w = sk ? rank_word(sk, p.part_idx[slot]) : 0ull;
     }
-    L.cand[j] = w;  // zero past |S|, as rank_in_lds needs
+    if (j < kSelCand) L.cand[j] = w;  // zero past |S|, as rank_in_lds needs
     if (j == 0) sh.thr = 0u;
     __syncthreads();
     uint64_t ws;
     uint32_t ci, part;
-    const uint32_t r = rank_in_lds(L.cand, (uint32_t)ns, ws, ci, part);
+    const uint32_t r = rank_in_lds<NT>(L.cand, (uint32_t)ns, ws, ci, part);
     if (part == 0 && ci < (uint32_t)ns && ws != 0ull && r == (uint32_t)p.k - 1) sh.thr = word_key(ws);
     __syncthreads();  // also: every read of L.cand is done before select_ordered clears it
     tmin = sh.thr;
   }
-  const int got = select_ordered<E, false>(key, idx, idx, idx, (uint32_t)p.k, sh, L, tmin);
-  for (int r = threadIdx.x; r < p.k; r += kSelThreads) {
+  const int got = select_ordered<E, false, NT>(key, idx, idx, idx, (uint32_t)p.k, sh, L, tmin);
+  for (int r = threadIdx.x; r < p.k; r += NT) {
     const bool ok = r < got;
     const int j = ok ? L.ord[r] : 0;
     p.out_token[row * p.k + r] = ok ? L.idx[j] : -1;
@@ -659,9 +694,10 @@ struct ExpandParams {
 
 // grid (S): scores of every (parent slot p, candidate c) child, index p * k + c,
 // and the w best by (score desc, index asc), written in that order. E slots
-// per thread (E * 256 >= w_prev * k).
+// per thread (E * kSelThreads >= w_prev * k).
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams p) {
+  constexpr int NT = kSelThreads;
   __shared__ SelShared sh;
   __shared__ SelLds L;
   const int64_t s = blockIdx.x;
@@ -671,7 +707,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
   const int M = p.w_prev * p.k;
   // a contiguous run of children per thread (each parent's candidates come
   // sorted, so a run mixes ranks, which keeps select_ordered's filter tight)
-  const int per = (M + kSelThreads - 1) / kSelThreads;  // <= E
+  const int per = (M + NT - 1) / NT;  // <= E
   uint32_t key[E];
   int32_t idx[E], tok[E];
 #pragma unroll
@@ -689,9 +725,9 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
     key[e] = (in && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = in ? j : -1;
   }
-  const int got = select_ordered<E, true>(key, idx, tok, tok, (uint32_t)p.w, sh, L);
+  const int got = select_ordered<E, true, NT>(key, idx, tok, tok, (uint32_t)p.w, sh, L);
   const int64_t o = s * p.out_stride;
-  for (int r = threadIdx.x; r < p.w; r += kSelThreads) {
+  for (int r = threadIdx.x; r < p.w; r += NT) {
     const bool ok = r < got;
     const int j = ok ? L.ord[r] : 0;
     const int child = ok ? L.idx[j] : 0;
@@ -719,9 +755,10 @@ struct PruneParams {
 
 // grid (S): the best `budget` supertree nodes by (score desc, depth asc, slot
 // asc) -- node index (d - 1) * w + slot orders depth, then slot -- flattened
-// after the root in that order. E slots per thread (E * 256 >= depths * w).
+// after the root in that order. E slots per thread (E * kPruneThreads >= depths * w).
 template <int E>
-__global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p) {
+__global__ __launch_bounds__(kPruneThreads) void prune_kernel(const PruneParams p) {
+  constexpr int NT = kPruneThreads;
   __shared__ SelShared sh;
   __shared__ SelLds L;
   __shared__ int16_t newpos[kSelMaxCand];  // supertree node -> row in the output (-1: not kept)
@@ -735,7 +772,7 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
   int32_t idx[E], tok[E], par[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = threadIdx.x + kSelThreads * e;
+    const int j = threadIdx.x + NT * e;
     const bool in = j < M;
     const float sc = in ? ssc[j] : -INFINITY;
     par[e] = in ? spar[j] : -1;
@@ -743,15 +780,15 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
     key[e] = (in && par[e] >= 0 && par[e] < p.w && isfinite(sc)) ? float_key(sc) : 0u;
     idx[e] = j;
   }
-  for (int j = threadIdx.x; j < M; j += kSelThreads) newpos[j] = -1;
+  for (int j = threadIdx.x; j < M; j += NT) newpos[j] = -1;
   if (threadIdx.x == 0) bad = 0;
-  const int got = select_ordered<E, true>(key, idx, tok, par, (uint32_t)p.budget, sh, L);
-  for (int r = threadIdx.x; r < got; r += kSelThreads) newpos[L.idx[L.ord[r]]] = (int16_t)(r + 1);
+  const int got = select_ordered<E, true, NT>(key, idx, tok, par, (uint32_t)p.budget, sh, L);
+  for (int r = threadIdx.x; r < got; r += NT) newpos[L.idx[L.ord[r]]] = (int16_t)(r + 1);
   __syncthreads();
   // With beta <= 0 and log-probabilities <= 0 a child never precedes its parent
   // (Lemma 1); check it, and if the data break it keep only nodes whose parent
   // is kept before them.
-  for (int r = threadIdx.x; r < got; r += kSelThreads) {
+  for (int r = threadIdx.x; r < got; r += NT) {
     const int j = L.ord[r];
     const int node = L.idx[j];
     if (node >= p.w) {  // depth > 1
@@ -788,7 +825,7 @@ __global__ __launch_bounds__(kSelThreads) void prune_kernel(const PruneParams p)
     p.score[o] = 0.f;
     p.n_out[s] = kept + 1;
   }
-  for (int r = threadIdx.x; r < p.budget; r += kSelThreads) {
+  for (int r = threadIdx.x; r < p.budget; r += NT) {
     const int64_t row = o + 1 + r;
     if (r < kept) {
       const int j = L.ord[r];
@@ -866,21 +903,22 @@ extern "C" int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = aligned(logits, 16) && row_stride % 4 == 0;
   const dim3 cgrid((unsigned)chunks, (unsigned)rows);
-  constexpr int kEL = kTopkChunkLarge / kSelThreads, kES = kTopkChunkSmall / kSelThreads;
+  constexpr int kEL = kTopkChunkLarge / kChunkThreads, kES = kTopkChunkSmall / kChunkThreads;
   if (topk_chunk_len(rows) == kTopkChunkLarge) {
-    if (vec) hipLaunchKernelGGL((topk_chunks<true, kEL>), cgrid, dim3(kSelThreads), 0, s, p);
-    else hipLaunchKernelGGL((topk_chunks<false, kEL>), cgrid, dim3(kSelThreads), 0, s, p);
+    if (vec) hipLaunchKernelGGL((topk_chunks<true, kEL>), cgrid, dim3(kChunkThreads), 0, s, p);
+    else hipLaunchKernelGGL((topk_chunks<false, kEL>), cgrid, dim3(kChunkThreads), 0, s, p);
   } else {
-    if (vec) hipLaunchKernelGGL((topk_chunks<true, kES>), cgrid, dim3(kSelThreads), 0, s, p);
-    else hipLaunchKernelGGL((topk_chunks<false, kES>), cgrid, dim3(kSelThreads), 0, s, p);
+    if (vec) hipLaunchKernelGGL((topk_chunks<true, kES>), cgrid, dim3(kChunkThreads), 0, s, p);
+    else hipLaunchKernelGGL((topk_chunks<false, kES>), cgrid, dim3(kChunkThreads), 0, s, p);
   }
   const int64_t M = (int64_t)chunks * k;
-  if (M <= 4 * kSelThreads)
-    hipLaunchKernelGGL(topk_merge<4>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
-  else if (M <= 16 * kSelThreads)
-    hipLaunchKernelGGL(topk_merge<16>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+  constexpr int kM0 = 1024 / kMergeThreads, kM1 = 4096 / kMergeThreads, kM2 = kSelMaxCand / kMergeThreads;
+  if (M <= kM0 * kMergeThreads)
+    hipLaunchKernelGGL(topk_merge<kM0>, dim3((unsigned)rows), dim3(kMergeThreads), 0, s, p);
+  else if (M <= kM1 * kMergeThreads)
+    hipLaunchKernelGGL(topk_merge<kM1>, dim3((unsigned)rows), dim3(kMergeThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(topk_merge<kSelPerThread>, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(topk_merge<kM2>, dim3((unsigned)rows), dim3(kMergeThreads), 0, s, p);
   return launch_status();
 }
 
@@ -958,11 +996,12 @@ extern "C" int dt_prune_topb(int32_t num_seqs, int32_t depths, int32_t w, int32_
   p.budget = budget;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t M = (int64_t)depths * w;
-  if (M <= 4 * kSelThreads)
-    hipLaunchKernelGGL(prune_kernel<4>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
-  else if (M <= 16 * kSelThreads)
-    hipLaunchKernelGGL(prune_kernel<16>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+  constexpr int kP0 = 1024 / kPruneThreads, kP1 = 4096 / kPruneThreads, kP2 = kSelMaxCand / kPruneThreads;
+  if (M <= kP0 * kPruneThreads)
+    hipLaunchKernelGGL(prune_kernel<kP0>, dim3((unsigned)num_seqs), dim3(kPruneThreads), 0, st, p);
+  else if (M <= kP1 * kPruneThreads)
+    hipLaunchKernelGGL(prune_kernel<kP1>, dim3((unsigned)num_seqs), dim3(kPruneThreads), 0, st, p);
   else
-    hipLaunchKernelGGL(prune_kernel<kSelPerThread>, dim3((unsigned)num_seqs), dim3(kSelThreads), 0, st, p);
+    hipLaunchKernelGGL(prune_kernel<kP2>, dim3((unsigned)num_seqs), dim3(kPruneThreads), 0, st, p);
   return launch_status();
 }
