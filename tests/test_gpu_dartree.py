@@ -150,7 +150,8 @@ def _random_layers(r, depths, w, k, beta, ties):
 
 @pytest.mark.parametrize("S,depths,w,k,budget,beta,ties", [(1, 16, 12, 64, 64, -0.2, False), (3, 16, 12, 64, 64, 0.0, True),
                                                            (2, 5, 8, 3, 1000, -0.2, False), (2, 16, 64, 64, 255, -0.2, False),
-                                                           (4, 3, 4, 2, 0, -0.2, False), (2, 16, 1024, 8, 1023, -0.1, False)])
+                                                           (4, 3, 4, 2, 0, -0.2, False), (2, 16, 1024, 8, 1023, -0.1, False),
+                                                           (2, 16, 200, 16, 300, -0.2, True)])
 def test_prune_matches_oracle(S, depths, w, k, budget, beta, ties):
     import torch
 
