@@ -6,7 +6,7 @@
 // All three are selections "the best m of M candidates" under a total order
 // (value descending, then a candidate index ascending). Two block-wide routines
 // do them. select_ordered first filters: a threshold that provably admits the
-// best m (from the waves' sorted per-thread bests, or a caller's hint) leaves a
+// best m (from the waves' per-thread bests, or a caller's hint) leaves a
 // few candidates, each ranked against the others, which yields them in order.
 // When more than 256 pass, a most-significant-digit radix select (four 8-bit
 // passes with an LDS histogram) finds the m-th best value, a
@@ -322,33 +322,6 @@ __device__ inline uint32_t lane_xor(uint32_t v) {
   else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), (int)v);
 }
 
-// Bitonic sort of the wave's 64 values (one per lane), largest in lane 0.
-__device__ inline uint32_t wave_sort_desc(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-  auto step = [&](auto JJ, int k) __attribute__((always_inline)) {
-    constexpr int J = decltype(JJ)::value;
-    const uint32_t o = lane_xor<J>(v);
-    // within a block of k lanes sorted descending when (lane & k) == 0: the
-    // lower lane of a pair keeps the larger value
-    const bool lower = (lane & J) == 0;
-    const bool desc = (lane & k) == 0;
-    v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
-  };
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I4 = std::integral_constant<int, 4>;
-  using I8 = std::integral_constant<int, 8>;
-  using I16 = std::integral_constant<int, 16>;
-  using I32 = std::integral_constant<int, 32>;
-  step(I1{}, 2);
-  step(I2{}, 4), step(I1{}, 4);
-  step(I4{}, 8), step(I2{}, 8), step(I1{}, 8);
-  step(I8{}, 16), step(I4{}, 16), step(I2{}, 16), step(I1{}, 16);
-  step(I16{}, 32), step(I8{}, 32), step(I4{}, 32), step(I2{}, 32), step(I1{}, 32);
-  step(I32{}, 64), step(I16{}, 64), step(I8{}, 64), step(I4{}, 64), step(I2{}, 64), step(I1{}, 64);
-  return v;
-}
-
 // Inclusive prefix sum over the wave's 64 lanes: shifts by 1, 2, 4 and 8
 // within each 16-lane row (lanes shifted in from outside the row add 0), then
 // the row totals carried forward by the row broadcasts of lanes 15 and 31.
@@ -364,6 +337,21 @@ __device__ inline uint32_t wave_incl_sum(uint32_t v) {
   v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
   v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
+}
+
+// The q-th largest of the wave's 64 values (1 <= q <= 64; counted with
+// multiplicity): the largest t with at least q lanes holding a value >= t,
+// built bit by bit from the top with one ballot per bit. 0 when fewer than q
+// lanes hold a non-zero value.
+__device__ inline uint32_t wave_qth_largest(uint32_t v, uint32_t q) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    const uint64_t in = __ballot(v >= c);
+    t = (uint32_t)__builtin_popcountll(in) >= q ? c : t;
+  }
+  return t;
 }
 
 // (key, index) as one 64-bit word that orders as (key desc, index asc) does;
@@ -409,18 +397,18 @@ __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& 
 // count (min(m, candidates), uniform across the block) and L.ord[r] = r.
 //
 // Most selections have few contenders near the top, so a filter comes first.
-// With NT threads, i.e. W = NT / 64 waves, every wave sorts its 64 threads' own
-// best keys; with q = ceil(m / W), let t be the smallest q-th largest among the
-// F waves that have q non-empty threads. Their q best thread keys are F q
-// distinct candidates with keys >= t, so when F q >= m the m-th best key is
-// >= t and every one of the best m passes the filter key >= t (otherwise t =
-// 1: every candidate passes). When at
-// most 256 candidates pass, each is ranked against all the others (its rank is
-// its position in the order; indices are unique, so ranks are distinct);
+// With NT threads, i.e. W = NT / 64 waves, every wave finds the q-th largest of
+// its 64 threads' own best keys, q = ceil(m / W) (wave_qth_largest); let t be
+// the smallest of these among the F waves that have q non-empty threads. Their
+// q best thread keys are F q distinct candidates with keys >= t, so when F q >=
+// m the m-th best key is >= t and every one of the best m passes the filter
+// key >= t (otherwise t = 1: every candidate passes). When at most 256
+// candidates pass, each is ranked against all the others (its rank is its
+// position in the order; indices are unique, so ranks are distinct);
 // otherwise the radix select and the sort below run as usual.
 //
 // A caller that knows a valid threshold (one with at least m candidates at
-// or above it) passes it as `hint` (0: none), and the waves' sort is skipped.
+// or above it) passes it as `hint` (0: none), and the waves' search is skipped.
 // Passing candidates get their slots from a prefix sum over each wave and one
 // LDS atomic per wave; the slots past the last candidate stay 0, so the
 // ranking (rank_in_lds) reads whole groups of eight with no bounds checks.
@@ -441,8 +429,7 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
     uint32_t best = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
-    const uint32_t sorted = wave_sort_desc(best);
-    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)(q - 1));  // 0: under q non-empty threads
+    const uint32_t tw = wave_qth_largest(best, q);  // 0: under q non-empty threads
     if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tw;
     __syncthreads();
     uint32_t t = 0xFFFFFFFFu, full = 0;
