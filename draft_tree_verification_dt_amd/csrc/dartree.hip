@@ -339,19 +339,31 @@ __device__ inline uint32_t wave_incl_sum(uint32_t v) {
   return v;
 }
 
-// The q-th largest of the wave's 64 values (1 <= q <= 64; counted with
-// multiplicity): the largest t with at least q lanes holding a value >= t,
-// built bit by bit from the top with one ballot per bit. 0 when fewer than q
-// lanes hold a non-zero value.
-__device__ inline uint32_t wave_qth_largest(uint32_t v, uint32_t q) {
-  uint32_t t = 0;
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    const uint64_t in = __ballot(v >= c);
-    t = (uint32_t)__builtin_popcountll(in) >= q ? c : t;
-  }
-  return t;
+// Bitonic sort of the wave's 64 values (one per lane), largest in lane 0.
+__device__ inline uint32_t wave_sort_desc(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+  auto step = [&](auto JJ, int k) __attribute__((always_inline)) {
+    constexpr int J = decltype(JJ)::value;
+    const uint32_t o = lane_xor<J>(v);
+    // within a block of k lanes sorted descending when (lane & k) == 0: the
+    // lower lane of a pair keeps the larger value
+    const bool lower = (lane & J) == 0;
+    const bool desc = (lane & k) == 0;
+    v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  using I32 = std::integral_constant<int, 32>;
+  step(I1{}, 2);
+  step(I2{}, 4), step(I1{}, 4);
+  step(I4{}, 8), step(I2{}, 8), step(I1{}, 8);
+  step(I8{}, 16), step(I4{}, 16), step(I2{}, 16), step(I1{}, 16);
+  step(I16{}, 32), step(I8{}, 32), step(I4{}, 32), step(I2{}, 32), step(I1{}, 32);
+  step(I32{}, 64), step(I16{}, 64), step(I8{}, 64), step(I4{}, 64), step(I2{}, 64), step(I1{}, 64);
+  return v;
 }
 
 // (key, index) as one 64-bit word that orders as (key desc, index asc) does;
@@ -397,18 +409,20 @@ __device__ inline uint32_t rank_in_lds(const uint64_t* w, uint32_t n, uint64_t& 
 // count (min(m, candidates), uniform across the block) and L.ord[r] = r.
 //
 // Most selections have few contenders near the top, so a filter comes first.
-// With NT threads, i.e. W = NT / 64 waves, every wave finds the q-th largest of
-// its 64 threads' own best keys, q = ceil(m / W) (wave_qth_largest); let t be
-// the smallest of these among the F waves that have q non-empty threads. Their
-// q best thread keys are F q distinct candidates with keys >= t, so when F q >=
-// m the m-th best key is >= t and every one of the best m passes the filter
-// key >= t (otherwise t = 1: every candidate passes). When at most 256
+// With NT threads, i.e. W = NT / 64 waves, every wave sorts its 64 threads' own
+// best keys. With q = ceil(m / W), let t be the smallest q-th largest among the
+// F waves that have q non-empty threads: their q best thread keys are F q
+// distinct candidates with keys >= t, so when F q >= m the m-th best key is
+// >= t and every one of the best m passes the filter key >= t (otherwise t =
+// 1: every candidate passes). Any one wave's m-th largest (m <= 64) is also a
+// valid threshold, since that wave alone has m candidates at or above it; the
+// filter takes the larger of the two. When at most 256
 // candidates pass, each is ranked against all the others (its rank is its
 // position in the order; indices are unique, so ranks are distinct);
 // otherwise the radix select and the sort below run as usual.
 //
 // A caller that knows a valid threshold (one with at least m candidates at
-// or above it) passes it as `hint` (0: none), and the waves' search is skipped.
+// or above it) passes it as `hint` (0: none), and the waves' sort is skipped.
 // Passing candidates get their slots from a prefix sum over each wave and one
 // LDS atomic per wave; the slots past the last candidate stay 0, so the
 // ranking (rank_in_lds) reads whole groups of eight with no bounds checks.
@@ -429,17 +443,26 @@ __device__ int select_ordered(const uint32_t (&key)[E], const int32_t (&idx)[E],
     uint32_t best = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
-    const uint32_t tw = wave_qth_largest(best, q);  // 0: under q non-empty threads
-    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = tw;
+    // tw: the wave's q-th best thread key; tm: its m-th best (m <= 64), which
+    // alone has m candidates at or above it (0 when it does not exist)
+    const uint32_t sorted = wave_sort_desc(best);
+    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)(q - 1));
+    const uint32_t tm = m <= 64 ? (uint32_t)__builtin_amdgcn_readlane((int)sorted, (int)(m - 1)) : 0u;
+    if ((threadIdx.x & 63) == 0) {
+      sh.red[threadIdx.x >> 6] = tw;
+      sh.hist[threadIdx.x >> 6] = tm;
+    }
     __syncthreads();
-    uint32_t t = 0xFFFFFFFFu, full = 0;
+    uint32_t t = 0xFFFFFFFFu, full = 0, t_one = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const uint32_t tv = sh.red[w];
       full += tv ? 1u : 0u;
       t = (tv && tv < t) ? tv : t;
+      t_one = sh.hist[w] > t_one ? sh.hist[w] : t_one;
     }
-    thr = full * q >= m ? t : 1u;
+    const uint32_t t_all = full * q >= m ? t : 1u;
+    thr = t_one > t_all ? t_one : t_all;
   } else {
     __syncthreads();
   }
