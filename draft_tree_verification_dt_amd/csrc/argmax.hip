@@ -351,15 +351,16 @@ __global__ __launch_bounds__(256) void argmax_merge(int64_t rows, int64_t vocab,
 // kernel runs. Greedy: 1024 threads with 4 loads in flight each (64 KB per
 // workgroup: with a workgroup on every CU that is about what HBM needs in
 // flight; four waves per SIMD measured 1-2 % faster than 512 threads with 8
-// loads each). Sampling: the same below eight rows per CU (there the Philox
-// arithmetic of some waves also overlaps the loads of others), and 256-thread
-// workgroups from eight rows per CU on, where several workgroups share each
-// CU. Fewer rows than CUs are cut into chunks of 256-thread workgroups and
-// merged.
+// loads each). Sampling, below eight rows per CU: 512 threads with 2 loads
+// each, double-buffered (the Philox arithmetic dominates; fewer registers per
+// wave let more rows share a CU and some waves' arithmetic overlap others'
+// loads: 4 % faster than 1024 x 4 at 256 rows, 8 % at 1024). From eight rows
+// per CU on, 256-thread workgroups. Fewer rows than CUs are cut into chunks of
+// 256-thread workgroups and merged.
 constexpr int kWideThreads = 1024;
 constexpr int kWideUnroll = 4;
-constexpr int kSampleWideThreads = 1024;
-constexpr int kSampleWideUnroll = 4;
+constexpr int kSampleWideThreads = 512;
+constexpr int kSampleWideUnroll = 2;
 
 int plan_chunks(int64_t rows, int64_t vocab, int cus, int64_t* chunk_len, int* chunks) {
   if (rows >= cus) {
