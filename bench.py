@@ -310,18 +310,21 @@ def time_on_stream(rnd, fn, reps):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def time_back_to_back(rnd, fn, reps):
+def time_back_to_back(rnd, fn, reps, ahead=2):
     """Mean GPU time of fn() in ms over `reps` consecutive calls bracketed by
     one pair of HIP events on the library's stream (the method of the
     attention calls' launch_us_mean): the kernels' own rate, without the gap
-    that an event pair around a single call adds. Two attention calls are
-    queued ahead of the start event; one untimed call comes first."""
+    that an event pair around a single call adds. `ahead` attention calls are
+    queued ahead of the start event, so that the host has enqueued every timed
+    call before the GPU reaches them (more for calls through the Python
+    binding, whose host time exceeds a small kernel's); one untimed call comes
+    first."""
     torch = rnd.torch
     fn(0)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    rnd.attention(0)
-    rnd.attention(1 % rnd.w.layers)
+    for l in range(ahead):
+        rnd.attention(l % rnd.w.layers)
     a.record()
     for i in range(reps):
         fn(i)
@@ -562,9 +565,12 @@ class DraftBuild:
 def time_draft_build(rnd, reps=10):
     db = DraftBuild(rnd.w, rnd.dev)
     topk_ms = time_on_stream(rnd, lambda i: db.topk(), reps)
+    topk_b2b = time_back_to_back(rnd, lambda i: db.topk(), 20, ahead=16)
     db.chain()  # every layer filled, so each timed expansion selects from real scores
     exp_ms = time_on_stream(rnd, lambda i: db.expand(1 + i % (db.GAMMA - 1)), reps)
+    exp_b2b = time_back_to_back(rnd, lambda i: db.expand(1 + i % (db.GAMMA - 1)), 20, ahead=16)
     prune_ms = time_on_stream(rnd, lambda i: db.prune(), reps)
+    prune_b2b = time_back_to_back(rnd, lambda i: db.prune(), 20, ahead=16)
     chain_ms = time_on_stream(rnd, lambda i: db.chain(), reps)
     # the same chain from one HIP graph: no host launch gaps between its 18 kernels
     torch = rnd.torch
@@ -576,8 +582,12 @@ def time_draft_build(rnd, reps=10):
     depth = db.tree[2].cpu().numpy()[0, :n_out]
     topk_bytes = db.GAMMA * rnd.w.vocab * 4
     return db, {"config": f"gamma {db.GAMMA}, vocab {rnd.w.vocab}, K {db.K}, W {db.W}, beta {db.BETA}, B {db.B}",
+            "timing": "single call between an event pair (topk_us, expand_us, prune_us); consecutive calls "
+                      "(*_us_back_to_back); the chain call by call and replayed from one HIP graph",
             "topk_us": topk_ms * 1e3, "topk_GB/s": topk_bytes / (topk_ms / 1e3) / 1e9,
-            "expand_us": exp_ms * 1e3, "prune_us": prune_ms * 1e3,
+            "topk_us_back_to_back": topk_b2b * 1e3,
+            "expand_us": exp_ms * 1e3, "expand_us_back_to_back": exp_b2b * 1e3,
+            "prune_us": prune_ms * 1e3, "prune_us_back_to_back": prune_b2b * 1e3,
             "chain_us": chain_ms * 1e3, "chain_graph_us": graph_ms * 1e3, "tree_nodes": n_out,
             "tree_max_depth": int(depth.max())}
 
