@@ -728,7 +728,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(const ExpandParams 
     tok[e] = -1;
     if (in) {
       const int par = j / p.k;
-      const float a = ps[par] + lq[j];  // Algorithm 1, line 8, in this order
+      const float a = ps[par] + lq[j];  // Algorithm 1's score update (eq. 5), in this order
       sc = a + p.beta;
       tok[e] = ct[j - par * p.k];
     }

@@ -379,7 +379,7 @@ int dt_commit_kv(const dt_commit_desc* desc, const void* const* k_tree, const vo
  * depth-wise fixed-width expansion and the deferred top-B pruning of DARTree
  * paper, Methodology (Depth-Wise Parallel Supertree Construction, Algorithm 1;
  * Deferred Best-First Pruning, eq. 5-6 and Lemma 1). The correction head that
- * scores candidates under each prefix (Algorithm 1, lines 5-6) is a trained
+ * scores candidates under each prefix (Algorithm 1's correction step) is a trained
  * network and stays with the caller: it turns the retained prefixes of depth
  * d-1 into log q~ values for every (prefix, candidate) pair, which
  * dt_expand_depth consumes.
@@ -396,7 +396,7 @@ int dt_topk_rows_workspace_size(int64_t rows, int64_t vocab, int32_t k, size_t* 
  *
  * Defined by: DARTree paper, Depth-Wise Parallel Supertree Construction (only
  * the drafter's top-K token predictions at each position are candidate
- * extensions) and Algorithm 1, line 4. Per row r: out_token[r][0..k-1] are the
+ * extensions) and Algorithm 1's candidate step. Per row r: out_token[r][0..k-1] are the
  * indices of the k largest logits ordered by (logit descending, index
  * ascending; -0 == +0), and out_logprob[r][j] = logits[r][out_token[r][j]] -
  * log(sum_v exp(logits[r][v])) in fp32. The same table, one row per draft
@@ -415,7 +415,7 @@ int dt_topk_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_s
 /*
  * dt_expand_depth -- one depth of DARTree's fixed-width supertree (GPU).
  *
- * Defined by: DARTree paper, Algorithm 1, lines 7-9, with eq. 5's score. For
+ * Defined by: DARTree paper, Algorithm 1's expansion step with eq. 5's score. For
  * every sequence s, every retained prefix (slot p < w_prev of depth d-1, score
  * parent_score[p]) and every candidate c < k of depth d, the child scores
  *   score(p, c) = (parent_score[p] + child_logq[p][c]) + beta      (fp32, in this order)
@@ -447,7 +447,7 @@ int dt_expand_depth(int32_t num_seqs, int32_t w_prev, int32_t k, int32_t w, floa
  *
  * Defined by: DARTree paper, Deferred Best-First Pruning, eq. 6 and Lemma 1
  * (with beta <= 0 and ancestors preferred on ties, the best-first heap over the
- * supertree equals its global top-B by s_beta), and Algorithm 1, line 12.
+ * supertree equals its global top-B by s_beta), and Algorithm 1's final pruning.
  * The supertree of sequence s is depths layers of w slots (dt_expand_depth's
  * outputs, layer d-1 at offset (d-1)*w): slot j of depth d is the child of slot
  * sel_parent of depth d-1 (depth 1: of the root), carries sel_token and

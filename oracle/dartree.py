@@ -64,7 +64,7 @@ def child_scores(parent_score, child_logq, beta):
 
 
 def expand_depth(parent_score, child_logq, beta, w):
-    """Algorithm 1, lines 7-9 for one sequence: score every (parent slot p,
+    """Algorithm 1's expansion step for one sequence: score every (parent slot p,
     candidate c) child and keep the w best by (score desc, p asc, c asc).
     Parents with score -inf (absent slots) have no children. Returns
     (parent slot, candidate index, score) lists of length <= w."""
