@@ -109,12 +109,17 @@ def _random_expand_case(r, S, w_prev, k, ties):
                                                      (2, 64, 256, 1024, -0.2, False), (2, 64, 256, 100, 0.0, True),
                                                      (5, 7, 9, 1, -0.2, True)])
 def test_expand_matches_oracle(S, w_prev, k, w, beta, ties):
-    import torch
-
     require_gpu()
     r = grng.stream(S, w_prev, k, w, "expand-gpu")
     ps, lq, ct = _random_expand_case(r, S, w_prev, k, ties)
     print(f"expand S={S} w_prev={w_prev} k={k} w={w} beta={beta} ties={ties}", flush=True)
+    _check_expand(ps, lq, ct, w, beta)
+
+
+def _check_expand(ps, lq, ct, w, beta):
+    import torch
+
+    S = ps.shape[0]
     par, cand, tok, sc = dt.dt_expand_depth(_t(ps), _t(lq), _t(ct), w, beta)
     torch.cuda.synchronize()
     par, cand, tok, sc = (x.cpu().numpy() for x in (par, cand, tok, sc))
@@ -153,15 +158,19 @@ def _random_layers(r, depths, w, k, beta, ties):
                                                            (4, 3, 4, 2, 0, -0.2, False), (2, 16, 1024, 8, 1023, -0.1, False),
                                                            (2, 16, 200, 16, 300, -0.2, True)])
 def test_prune_matches_oracle(S, depths, w, k, budget, beta, ties):
-    import torch
-
     require_gpu()
     r = grng.stream(S, depths, w, budget, "prune-gpu")
+    print(f"prune S={S} depths={depths} w={w} budget={budget} ties={ties}", flush=True)
+    _check_prune(r, S, depths, w, k, budget, beta, ties)
+
+
+def _check_prune(r, S, depths, w, k, budget, beta, ties):
+    import torch
+
     layers = [_random_layers(r, depths, w, k, beta, ties) for _ in range(S)]
     ctok = [r.integers(0, 151936, size=(depths, k)) for _ in range(S)]
     par, tok, sc = _layers_to_arrays(layers, depths, w, ctok)
     roots = r.integers(0, 151936, size=S).astype(np.int32)
-    print(f"prune S={S} depths={depths} w={w} budget={budget} ties={ties}", flush=True)
     gp, gt, gd, gs, gn = dt.dt_prune_topb(_t(par), _t(tok), _t(sc), _t(roots), budget)
     torch.cuda.synchronize()
     gp, gt, gd, gs, gn = (x.cpu().numpy() for x in (gp, gt, gd, gs, gn))
@@ -176,6 +185,45 @@ def test_prune_matches_oracle(S, depths, w, k, budget, beta, ties):
         np.testing.assert_array_equal(gs[s, :n].view(np.uint32), ws.view(np.uint32))
         assert (gp[s, n:] == -1).all() and (gd[s, n:] == -1).all()
         otree.check(gp[s, :n])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_selections_on_random_shapes(seed):
+    """Seeded random shapes for the three selections against the oracle: top-K
+    rows (either chunk length, every merge tier), one expansion depth and the
+    pruning, with and without heavy ties. Between them they cross the filter's
+    two threshold bounds, ranking with 2 to 8 lanes per candidate, and the
+    radix fallback when too many candidates pass."""
+    require_gpu()
+    r = grng.stream(seed, "selection-sweep")
+    for case in range(5):
+        rows = int(r.integers(1, 41))
+        vocab = int(r.choice([7, 1000, 4097, 30000, 151936, 262144]))
+        chunk_len = 10240 if rows >= 16 else 4096
+        kmax = min(vocab, 1024, 16384 // -(-vocab // chunk_len))
+        k = int(r.integers(1, kmax + 1))
+        x = (r.standard_normal((rows, vocab)) * 3).astype(np.float32)
+        if r.random() < 0.4:
+            x = (np.round(x * 2) / 2).astype(np.float32)  # few distinct levels: large ties
+        print(f"sweep {seed}.{case} topk rows={rows} vocab={vocab} k={k}", flush=True)
+        _check_topk(x, k)
+
+        S = int(r.integers(1, 5))
+        w_prev = int(r.integers(1, 65))
+        kk = int(r.integers(1, min(256, 16384 // w_prev) + 1))
+        w = int(r.integers(1, min(1024, w_prev * kk) + 1))
+        beta = float(r.choice([0.0, -0.2, -1.0]))
+        ties = bool(r.random() < 0.4)
+        print(f"sweep {seed}.{case} expand S={S} w_prev={w_prev} k={kk} w={w} beta={beta} ties={ties}", flush=True)
+        _check_expand(*_random_expand_case(r, S, w_prev, kk, ties), w, beta)
+
+        depths = int(r.integers(1, 17))
+        wd = int(r.integers(1, 257))
+        kd = int(r.integers(1, 65))
+        budget = int(r.integers(0, min(1023, depths * wd) + 1))
+        ties = bool(r.random() < 0.4)
+        print(f"sweep {seed}.{case} prune S={S} depths={depths} w={wd} k={kd} budget={budget} ties={ties}", flush=True)
+        _check_prune(r, S, depths, wd, kd, budget, -0.2, ties)
 
 
 def _synthetic_head(cand_logprob, paths, cands, strength=1.0):
