@@ -33,6 +33,24 @@ def test_argmax_random(rows, vocab):
     np.testing.assert_array_equal(_argmax_dev(x), oarg.argmax_rows(x))
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_argmax_random_shapes(seed):
+    """Seeded random row counts (across the chunked, the one-row-per-workgroup
+    and the many-rows-per-CU launches), vocabulary sizes (tails of every
+    length), row strides and tie structures, bit-exact against np.argmax."""
+    require_gpu()
+    r = grng.stream(seed, "argmax-sweep")
+    for case in range(6):
+        rows = int(r.choice([1, 7, 100, 255, 256, 257, 600, 2100]))
+        vocab = int(r.integers(1, max(2, min(200000, 8_000_000 // rows))))
+        pad = int(r.integers(0, 5))
+        x = r.standard_normal((rows, vocab), dtype=np.float32)
+        if r.random() < 0.4:
+            x = np.round(x).astype(np.float32)  # few distinct values: the lowest index must win
+        print(f"argmax sweep {seed}.{case} rows={rows} vocab={vocab} pad={pad}", flush=True)
+        np.testing.assert_array_equal(_argmax_dev(x, stride_pad=pad), oarg.argmax_rows(x))
+
+
 @pytest.mark.parametrize("pad", [1, 3, 4])
 def test_argmax_strided_rows(pad):
     require_gpu()

@@ -82,6 +82,24 @@ def test_sample_matches_oracle(rows, vocab, T):
     check_samples(_sample_dev(x, T, seed, offset), x, T, seed, offset)
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_sample_random_shapes(seed):
+    """Seeded random row counts (chunked, one 512-thread workgroup per row, and
+    256-thread workgroups from eight rows per CU on), vocabulary sizes, row
+    strides and temperatures against the oracle's perturbed scores."""
+    require_gpu()
+    r = grng.stream(seed, "sample-sweep")
+    for case in range(5):
+        rows = int(r.choice([1, 9, 255, 256, 700, 2100]))
+        vocab = int(r.integers(1, max(2, min(120000, 2_000_000 // rows))))
+        pad = int(r.integers(0, 5))
+        T = float(r.choice([0.3, 1.0, 1.7]))
+        x = (r.standard_normal((rows, vocab), dtype=np.float32) * np.float32(2.0))
+        seed_, offset = int(r.integers(0, 1 << 63)), int(r.integers(0, 1 << 63))
+        print(f"sample sweep {seed}.{case} rows={rows} vocab={vocab} pad={pad} T={T}", flush=True)
+        check_samples(_sample_dev(x, T, seed_, offset, stride_pad=pad), x, T, seed_, offset)
+
+
 @pytest.mark.parametrize("pad", [1, 3, 4])
 def test_sample_strided_rows(pad):
     """Row strides that are not a multiple of four take the scalar path; same draws."""
