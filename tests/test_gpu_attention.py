@@ -99,6 +99,32 @@ def test_sharp_distribution_and_custom_scale():
     assert_attention_close(host_f64(out2), _oracle(ops, parents, [100], [300], scale=0.05), what="scale")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_batches(seed):
+    """Seeded random batches: sequence counts, tree sizes and shapes, prefix
+    lengths (ragged or equal), GQA group sizes, head dims 64 and 128, and now
+    and then a forced key split, against the oracle. The planner picks its row
+    tiles, splits and launches on its own for each."""
+    require_gpu()
+    r = grng.stream(seed, "attention-sweep")
+    for case in range(4):
+        S = int(r.integers(1, 5))
+        nodes = [int(r.integers(1, 300)) for _ in range(S)]
+        if r.random() < 0.5:
+            plens = [int(r.integers(0, 2500)) for _ in range(S)]
+        else:
+            plens = [int(r.integers(0, 2500))] * S
+        Hkv, g = int(r.choice([1, 2, 4])), int(r.choice([1, 2, 3, 4, 8]))
+        d = int(r.choice([64, 128]))
+        split = int(r.choice([0, 0, 0, 64, 192, 1024]))
+        shapes = [str(r.choice(["recursive", "deep", "bfs", "chain", "heap"]))]
+        print(f"attention sweep {seed}.{case} S={S} n={nodes} P={plens} Hkv={Hkv} g={g} d={d} split={split} "
+              f"shape={shapes[0]}", flush=True)
+        parents, ops = _case(nodes, plens, Hkv * g, Hkv, d, shapes, seed=seed * 10 + case)
+        out, _ = _run(ops, parents, nodes, plens, Hkv * g, Hkv, d, split_keys=split)
+        assert_attention_close(host_f64(out), _oracle(ops, parents, nodes, plens), what=f"sweep {seed}.{case}")
+
+
 @pytest.mark.parametrize("split", [64, 128, 576, 4096])
 def test_forced_key_splits(split):
     require_gpu()
