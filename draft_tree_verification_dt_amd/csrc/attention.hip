@@ -86,7 +86,8 @@ struct SeqGeom {
   int32_t splits;       // key chunks
   int32_t row_tiles;    // ceil(n*g / rows per workgroup)
   int32_t item_start;   // first work item
-  int32_t part_base;    // first partial row (split sequences), else -1
+  int32_t part_base;    // first partial row (split sequences), else -1; the sequence's
+                        // partial rows go (key chunk, KV head, packed row node * g + j)
   int32_t comb_start;   // first combine row (split sequences)
 };
 
@@ -755,19 +756,19 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     return *reinterpret_cast<uint2*>(b4);
   };
   // first element of a row's output (bf16 O, or the fp16 partial of this split)
-  auto row_dst = [&](int node, int qh) __attribute__((always_inline)) -> uint16_t* {
-    return part ? reinterpret_cast<uint16_t*>(p.part_o) +
-                      ((int64_t)sg.part_base + ((int64_t)split * sg.n + node) * p.Hq + qh) * D
-                : p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D;
+  const int64_t part_row0 = (int64_t)sg.part_base + (int64_t)split * sg.n * p.Hq + (int64_t)head * nrows;
+  auto row_dst = [&](int row) __attribute__((always_inline)) -> uint16_t* {
+    return part ? reinterpret_cast<uint16_t*>(p.part_o) + (part_row0 + row) * D
+                : p.out + (int64_t)(sg.node_off + row / g) * p.out_rs + (int64_t)(head * g + row % g) * D;
   };
   if (part && row_ok && hh == 0) {
-    const int64_t prow = (int64_t)sg.part_base + ((int64_t)split * sg.n + my_node) * p.Hq + my_qh;
+    const int64_t prow = part_row0 + my_row;
     p.part_ml[prow] = make_float4(m_run, l_tot, __builtin_amdgcn_ldexpf(1.f, e), 0.f);
   }
 
   if constexpr (WN > 1) {
     // few rows per workgroup: every lane stores its own row's groups
-    uint16_t* orow = row_dst(my_node, my_qh);
+    uint16_t* orow = row_dst(my_row);
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 #pragma unroll
     for (int k = 0; k < kStores; ++k) {
       const int row = wrow0 + k * kRowsPerStore + sr;
-      if (row < nrows) *reinterpret_cast<u32x4*>(row_dst(row / g, head * g + row % g) + sc16 * 8) = v[k];
+      if (row < nrows) *reinterpret_cast<u32x4*>(row_dst(row) + sc16 * 8) = v[k];
     }
   }
 }
@@ -822,12 +823,16 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 // per (row, slice) that take every G-th chunk and merge their running (m, l, O)
 // through cross-lane shuffles at the end (for many chunks and few rows, so that
 // more threads carry the loads). The G * D/8 threads of a row are adjacent lanes
-// of one wave.
+// of one wave. Rows go in the partials' order, (KV head, node, query head within
+// the group), so a block's rows are contiguous in every chunk, and contiguous
+// ranges of blocks go to one XCD, as the forward kernel's work items do.
 template <int D, int G>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   constexpr int kTpr = D / 8;          // threads per row and chunk group
   constexpr int kRpb = 256 / (kTpr * G);  // rows per block
-  const int row = blockIdx.x * kRpb + threadIdx.x / (kTpr * G);
+  const int nbx = gridDim.x / kXcds;
+  const int cb = (blockIdx.x % kXcds) * nbx + blockIdx.x / kXcds;
+  const int row = cb * kRpb + threadIdx.x / (kTpr * G);
   const int gi = (threadIdx.x / kTpr) % G;
   const int c8 = threadIdx.x % kTpr;
   if (row >= p.comb_rows) return;  // the row's G * kTpr lanes leave together
@@ -836,10 +841,12 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
     if (p.seq[i].splits > 1 && p.seq[i].comb_start <= row) s = i;
   if (s < 0) return;
   const SeqGeom& sg = p.seq[s];
-  const int r = row - sg.comb_start;  // = node * Hq + qh
+  const int r = row - sg.comb_start;  // = (KV head * n + node) * g + j, for query head KV head * g + j
   if (r >= sg.n * p.Hq) return;
-  const int node = r / p.Hq, qh = r % p.Hq;
-  // partial row of chunk k: part_base + (k * n + node) * Hq + qh = part_base + r + k * n * Hq
+  const int ng = sg.n * p.g;
+  const int hkv = r / ng, rem = r - hkv * ng;
+  const int node = rem / p.g, qh = hkv * p.g + rem % p.g;
+  // partial row of chunk k: part_base + k * n * Hq + r (the order the forward kernel writes them in)
   const int64_t prow0 = (int64_t)sg.part_base + r;
   const int64_t kstride = (int64_t)sg.n * p.Hq;
   const uint4* po = reinterpret_cast<const uint4*>(p.part_o);  // eight fp16 values per thread
@@ -1095,7 +1102,7 @@ void plan_launch(const dt_attn_desc* d, const Plan& plan, int s0, size_t* part_r
   L->grid = a.per_xcd * kXcds;
   // many chunks per row: four threads share each (row, slice), more threads carry the loads
   L->comb_groups = max_splits > 8 ? 4 : 1;
-  L->comb_grid = comb ? (int)ceil_div(comb, 256 / (d->head_dim / 8 * L->comb_groups)) : 0;
+  L->comb_grid = comb ? (int)ceil_div(ceil_div(comb, 256 / (d->head_dim / 8 * L->comb_groups)), kXcds) * kXcds : 0;
   L->lds = dynamic_lds(launch_max_n, g, plan.wm);
 }
 
