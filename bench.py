@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="0: greedy verification (dt_argmax_rows); > 0: exact target-sample matching (dt_sample_rows)")
     ap.add_argument("--commit", action="store_true", help="commit the accepted K/V rows in every step")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="print the forward kernel's per-workgroup phase stamps for the workload and exit")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
@@ -562,6 +564,67 @@ class DraftBuild:
         self.prune()
 
 
+def phase_stamps(rnd, reps=24, rows=8192):
+    """Per-workgroup phase stamps (the descriptor's phase_stamps: the GPU's
+    100 MHz real-time counter at fixed points of every workgroup of the forward
+    and merge kernels) over `reps` consecutive calls that rotate through the
+    layer caches. Per call, times are taken from that call's first forward
+    workgroup entry: for each forward phase the median over the calls of the
+    median, minimum and maximum over workgroups; the merge kernel's first entry
+    and last store; and the gaps at the kernel boundaries (last forward store to
+    first merge entry, last merge store to the next call's first entry), in µs."""
+    import ctypes
+
+    torch, w = rnd.torch, rnd.w
+    bufs = torch.zeros((reps, rows, 8), dtype=torch.int64, device=rnd.dev)
+    descs = []
+    for i in range(reps):
+        d = type(rnd.desc).from_buffer_copy(rnd.desc)
+        d.phase_stamps = bufs[i].data_ptr()
+        d.phase_stamp_rows = rows
+        descs.append(d)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        st = rnd.lib.dt_tree_attention(ctypes.byref(descs[i]), *rnd.att_args[i % w.layers], rnd.stream)
+        if st != 0:
+            raise rnd.dt.DtError(st, "dt_tree_attention")
+    torch.cuda.synchronize()
+    s = bufs.cpu().numpy()
+    names = ["entry", "first_stage_requested", "setup_done", "first_stage_landed", "main_loop_done", "stored"]
+    per = {k: {"median": [], "min": [], "max": []} for k in names}
+    merge = {"first_entry": [], "last_stored": []}
+    gaps = {"forward_to_merge": [], "merge_to_next_call": [], "call_period": []}
+    wgs, mbs, spans = [], [], []
+    for i in range(reps):
+        f = s[i][(s[i][:, 7] == 1) & (s[i][:, 5] != 0)]  # forward workgroups that stored outputs
+        m = s[i][(s[i][:, 7] == 2) & (s[i][:, 5] != 0)]  # merge blocks that stored outputs
+        wgs.append(len(f))
+        mbs.append(len(m))
+        t0 = s[i][s[i][:, 7] == 1][:, 0].min()
+        for k, name in enumerate(names):
+            v = (f[:, k][f[:, k] != 0] - t0) / 100.0
+            per[name]["median"].append(np.median(v))
+            per[name]["min"].append(v.min())
+            per[name]["max"].append(v.max())
+        end = f[:, 5].max()
+        if len(m):
+            merge["first_entry"].append((m[:, 0].min() - t0) / 100.0)
+            merge["last_stored"].append((m[:, 5].max() - t0) / 100.0)
+            gaps["forward_to_merge"].append((m[:, 0].min() - f[:, 5].max()) / 100.0)
+            end = m[:, 5].max()
+        if i + 1 < reps:
+            t1 = s[i + 1][s[i + 1][:, 7] == 1][:, 0].min()
+            gaps["merge_to_next_call"].append((t1 - end) / 100.0)
+            gaps["call_period"].append((t1 - t0) / 100.0)
+    med = lambda x: round(float(np.median(x)), 2) if len(x) else None
+    return {"workload": w.name, "calls": reps, "forward_workgroups": int(np.median(wgs)),
+            "merge_blocks": int(np.median(mbs)),
+            "clock": "s_memrealtime, 100 MHz; µs after the call's first forward workgroup entry",
+            "forward_phases_us": {k: {m_: med(x) for m_, x in v.items()} for k, v in per.items()},
+            "merge_us": {k: med(v) for k, v in merge.items()},
+            "gaps_us": {k: med(v) for k, v in gaps.items()}}
+
+
 def time_draft_build(rnd, reps=10):
     db = DraftBuild(rnd.w, rnd.dev)
     topk_ms = time_on_stream(rnd, lambda i: db.topk(), reps)
@@ -765,6 +828,9 @@ def main():
     for _ in range(args.warmup):
         rnd.step()
     torch.cuda.synchronize()
+    if args.phase_stamps:
+        print(json.dumps(phase_stamps(rnd)), flush=True)
+        return
     # the timed region; HIP events on the kernels' stream bracket each step's attention calls
     att_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.steps)]

@@ -245,18 +245,26 @@ def _check_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out)
 
 
 def dt_tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, scale=None, split_keys=0,
-                      out=None, workspace=None, stream=None):
+                      out=None, workspace=None, stream=None, phase_stamps=None):
     """Ancestor-only tree attention (GPU).
 
     q [N, Hq, d], k_tree/v_tree [N, Hkv, d], k_prefix/v_prefix [rows, Hkv, d]
     (any row/head strides, d contiguous; may be None when every prefix is
     empty), parent int32 [N] tree-local, all torch CUDA tensors (bf16 for the
-    operands). Returns out [N, Hq, d] bf16.
+    operands). Returns out [N, Hq, d] bf16. phase_stamps (profiling, optional):
+    a contiguous int64 CUDA tensor [rows, 8] that receives every workgroup's
+    real-time counter stamps (the descriptor's phase_stamps).
     """
     import torch
 
     dev = _check_attention(q, k_tree, v_tree, k_prefix, v_prefix, parent, layout, out)
     desc = _attn_geometry(q, k_tree, k_prefix, layout, scale, split_keys)
+    if phase_stamps is not None:
+        _req(phase_stamps, "phase_stamps", torch.int64, dev)
+        if phase_stamps.dim() != 2 or phase_stamps.shape[1] != 8 or not phase_stamps.is_contiguous():
+            raise ValueError("phase_stamps: expected a contiguous [rows, 8] tensor")
+        desc.phase_stamps = phase_stamps.data_ptr()
+        desc.phase_stamp_rows = phase_stamps.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     _req_workspace(workspace, "workspace", dev)

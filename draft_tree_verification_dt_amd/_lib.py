@@ -47,6 +47,8 @@ class dt_attn_desc(ctypes.Structure):
         ("tree_row_stride", c_i64),
         ("prefix_row_stride", c_i64),
         ("prefix_head_stride", c_i64),
+        ("phase_stamps", ctypes.c_void_p),
+        ("phase_stamp_rows", c_i64),
     ]
 
 

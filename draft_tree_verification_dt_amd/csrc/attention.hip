@@ -76,6 +76,7 @@ constexpr int kStageBudget = 128 * 1024;  // LDS bytes for the K/V pipeline
 constexpr int kLdsBytes = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // log2 units a stale running max may lag the true one
+constexpr int kStampSlots = 8;          // phase-stamp slots per workgroup (slot 7: 1 forward, 2 merge)
 constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" for the running max
 
 struct SeqGeom {
@@ -112,6 +113,10 @@ struct AttnParams {
   int32_t mask_rows;    // rows of the ancestor-mask table (max nodes per row tile)
   int32_t max_n;
   int32_t comb_rows;
+  uint64_t* stamps;     // optional phase stamps, kStampSlots per row: the forward kernel's
+  int32_t stamp_wg0;    // workgroup b writes row stamp_wg0 + b, the merge kernel's block b
+  int32_t stamp_cb0;    // row stamp_cb0 + b; rows from stamp_rows on are not written
+  int32_t stamp_rows;
   SeqGeom seq[kMaxSeqs];
 };
 
@@ -212,7 +217,7 @@ __device__ inline float sum_halves(float v) {
   return h.x + h.y;
 }
 
-template <int D, int WM>
+template <int D, int WM, bool STAMPS>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p) {
   using T = Tile<D>;
   using SH = Shape<D, WM>;
@@ -235,6 +240,20 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     char* v;
   };
   extern __shared__ uint32_t dyn[];  // parents, ancestor masks, key-slice merge statistics
+
+  // Phase stamps (the STAMPS instantiation, for profiling only): lane 0 of
+  // wave 0 records the 100 MHz real-time counter at fixed points of the
+  // workgroup's life. The default instantiation has none of this code.
+  auto stamp = [&](int k) __attribute__((always_inline)) {
+    if constexpr (STAMPS) {
+      const int row = p.stamp_wg0 + (int)blockIdx.x;
+      if (threadIdx.x == 0 && row < p.stamp_rows) {
+        p.stamps[(int64_t)row * kStampSlots + k] = __builtin_amdgcn_s_memrealtime();
+        if (k == 0) p.stamps[(int64_t)row * kStampSlots + 7] = 1;
+      }
+    }
+  };
+  stamp(0);
 
   // ---- work item (XCD-aware remap: consecutive items share an XCD) ----
   const int b = blockIdx.x;
@@ -345,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   uint32_t par0 = 0;
   if (need_mask && tid <= node_hi) par0 = (uint32_t)p.parent[sg.node_off + tid];
   if (nsteps > 0) issue(key_lo, Stage{k0, v0});
+  stamp(1);
 
   // ---- Q rows (B operand of S^T = K Q^T): lane holds row lr, dims 16k + 8hh .. +7 ----
   bf16x8 qreg[KS];
@@ -585,6 +605,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     constexpr int u = decltype(U)::value;
     wait_step(step);
     stage_barrier();  // every wave's loads of this step have landed; everyone is done with step - 1
+    if (step == 0) stamp(3);
     if constexpr (NST > 1) {
       if (step + NST - 1 < nsteps)
         issue(key_lo + (step + NST - 1) * KN, stage_ptr(std::integral_constant<int, (u + NST - 1) % NST>{}));
@@ -596,6 +617,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     }
   };
 
+  stamp(2);
   if constexpr (NST == 4 && WN == 1) {
     // Ping-pong: waves 0-3 (group A, one per SIMD) and waves 4-7 (group B) take
     // turns. Every step has two phases, each closed by a workgroup barrier; in
@@ -628,6 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     auto group_a = [&](int s, auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       even_barrier(s, U);
+      if (s == 0) stamp(3);
       x_block(s, stage_ptr(U), stage_ptr(std::integral_constant<int, (u + 3) % 4>{}));
       stage_barrier();
       if (s + 2 < nsteps) issue(key_lo + (s + 2) * KN, stage_ptr(std::integral_constant<int, (u + 2) % 4>{}));
@@ -680,6 +703,8 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
     if constexpr (NST > 3) if (s0 + 3 < nsteps) run_step(s0 + 3, std::integral_constant<int, 3>{});
   }
   }
+
+  stamp(4);
 
   // ---- epilogue: lane (lr, hh) holds O^T[d][row lr] for d = 32i + 8(j/4) + 4hh + (j%4) ----
   float l_tot = sum_halves(l_run);
@@ -814,6 +839,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
       if (row < nrows) *reinterpret_cast<u32x4*>(row_dst(row) + sc16 * 8) = v[k];
     }
   }
+  stamp(5);
 }
 
 // Merge the per-chunk partials of split sequences. A thread owns eight
@@ -826,8 +852,20 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
 // of one wave. Rows go in the partials' order, (KV head, node, query head within
 // the group), so a block's rows are contiguous in every chunk, and contiguous
 // ranges of blocks go to one XCD, as the forward kernel's work items do.
-template <int D, int G>
+template <int D, int G, bool STAMPS>
 __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
+  // phase stamps (the STAMPS instantiation only): entry (slot 0) and output
+  // stored (slot 5) of lane 0 of the block
+  auto stamp = [&](int k) __attribute__((always_inline)) {
+    if constexpr (STAMPS) {
+      const int row = p.stamp_cb0 + (int)blockIdx.x;
+      if (threadIdx.x == 0 && row < p.stamp_rows) {
+        p.stamps[(int64_t)row * kStampSlots + k] = __builtin_amdgcn_s_memrealtime();
+        if (k == 0) p.stamps[(int64_t)row * kStampSlots + 7] = 2;
+      }
+    }
+  };
+  stamp(0);
   constexpr int kTpr = D / 8;          // threads per row and chunk group
   constexpr int kRpb = 256 / (kTpr * G);  // rows per block
   const int nbx = gridDim.x / kXcds;
@@ -913,6 +951,7 @@ __global__ __launch_bounds__(256) void tree_attn_combine(const AttnParams p) {
   for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(o[e] * inv);
   bf16_bits* orow = p.out + (int64_t)(sg.node_off + node) * p.out_rs + (int64_t)qh * D + c8 * 8;
   *reinterpret_cast<uint4*>(orow) = *reinterpret_cast<uint4*>(o8);
+  stamp(5);
 }
 
 // ---------------------------------------------------------------- host side
@@ -940,6 +979,7 @@ int check_desc(const dt_attn_desc* d) {
   if (d->num_q_heads % d->num_kv_heads) return DT_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return DT_ERR_UNSUPPORTED;
   if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale)) return DT_ERR_SHAPE;
+  if (d->phase_stamp_rows < 0 || (d->phase_stamps && !aligned(d->phase_stamps, 8))) return DT_ERR_SHAPE;
   if (d->split_keys < 0 || d->split_keys % kBN) return DT_ERR_SHAPE;
   if (!d->node_offsets || !d->prefix_lens || !d->prefix_row_start) return DT_ERR_NULL;
   if (d->node_offsets[0] != 0) return DT_ERR_SHAPE;
@@ -1155,14 +1195,34 @@ int make_plan(const dt_attn_desc* d, Plan* plan) {
   return DT_OK;
 }
 
-template <int D>
-void launch_fwd(int wm, int grid, size_t lds, hipStream_t st, const AttnParams& a) {
+template <int D, bool STAMPS>
+void launch_fwd_as(int wm, int grid, size_t lds, hipStream_t st, const AttnParams& a) {
   if (wm == 8)
-    hipLaunchKernelGGL((tree_attn_fwd<D, 8>), dim3(grid), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((tree_attn_fwd<D, 8, STAMPS>), dim3(grid), dim3(kThreads), lds, st, a);
   else if (wm == 4)
-    hipLaunchKernelGGL((tree_attn_fwd<D, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((tree_attn_fwd<D, 4, STAMPS>), dim3(grid), dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((tree_attn_fwd<D, 2>), dim3(grid), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((tree_attn_fwd<D, 2, STAMPS>), dim3(grid), dim3(kThreads), lds, st, a);
+}
+
+template <int D, bool STAMPS>
+void launch_kernels(const Launch& L, int wm, hipStream_t st) {
+  launch_fwd_as<D, STAMPS>(wm, L.grid, L.lds, st, L.a);
+  if (L.comb_grid) {
+    if (L.comb_groups > 1)
+      hipLaunchKernelGGL((tree_attn_combine<D, 4, STAMPS>), dim3(L.comb_grid), dim3(256), 0, st, L.a);
+    else
+      hipLaunchKernelGGL((tree_attn_combine<D, 1, STAMPS>), dim3(L.comb_grid), dim3(256), 0, st, L.a);
+  }
+}
+
+// One launch's kernels: the forward kernel, then the merge of split rows.
+template <int D>
+void launch_call(const Launch& L, int wm, hipStream_t st) {
+  if (L.a.stamps)
+    launch_kernels<D, true>(L, wm, st);
+  else
+    launch_kernels<D, false>(L, wm, st);
 }
 
 }  // namespace
@@ -1196,6 +1256,7 @@ int run_attention(const dt_attn_desc* desc, const Plan& plan, const void* q, con
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   size_t part_rows = 0;
+  int32_t stamp_wg0 = 0;
   Launch L;
   for (int s0 = 0; s0 < desc->num_seqs; s0 += kMaxSeqs) {
     plan_launch(desc, plan, s0, &part_rows, &L);
@@ -1214,24 +1275,16 @@ int run_attention(const dt_attn_desc* desc, const Plan& plan, const void* q, con
     a.t_rs = trs;
     a.p_rs = desc->prefix_row_stride;
     a.p_hs = desc->prefix_head_stride;
+    a.stamps = desc->phase_stamps;
+    a.stamp_rows = (int32_t)std::min<int64_t>(desc->phase_stamp_rows, INT32_MAX);
     if (a.total_items == 0) continue;
-    if (D == 128) {
-      launch_fwd<128>(plan.wm, L.grid, L.lds, st_, a);
-      if (L.comb_grid) {
-        if (L.comb_groups > 1)
-          hipLaunchKernelGGL((tree_attn_combine<128, 4>), dim3(L.comb_grid), dim3(256), 0, st_, a);
-        else
-          hipLaunchKernelGGL((tree_attn_combine<128, 1>), dim3(L.comb_grid), dim3(256), 0, st_, a);
-      }
-    } else {
-      launch_fwd<64>(plan.wm, L.grid, L.lds, st_, a);
-      if (L.comb_grid) {
-        if (L.comb_groups > 1)
-          hipLaunchKernelGGL((tree_attn_combine<64, 4>), dim3(L.comb_grid), dim3(256), 0, st_, a);
-        else
-          hipLaunchKernelGGL((tree_attn_combine<64, 1>), dim3(L.comb_grid), dim3(256), 0, st_, a);
-      }
-    }
+    a.stamp_wg0 = stamp_wg0;
+    a.stamp_cb0 = stamp_wg0 + L.grid;
+    stamp_wg0 += L.grid + L.comb_grid;
+    if (D == 128)
+      launch_call<128>(L, plan.wm, st_);
+    else
+      launch_call<64>(L, plan.wm, st_);
     const int st = launch_status();
     if (st != DT_OK) return st;
   }

@@ -36,7 +36,7 @@ extern "C" const char* dt_status_string(int status) {
   }
 }
 
-extern "C" int dt_abi_version(void) { return (1 << 16) | 0; }
+extern "C" int dt_abi_version(void) { return (2 << 16) | 0; }
 
 extern "C" int dt_validate_tree(const int32_t* parent, int32_t n) {
   if (n < 1) return DT_ERR_SHAPE;

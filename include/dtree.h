@@ -83,7 +83,7 @@ enum dt_status {
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* dt_status_string(int status);
 
-/* ABI version of this header: (major << 16) | minor. */
+/* ABI version of this header: (major << 16) | minor; 2.0 (dt_attn_desc gained phase_stamps). */
 int dt_abi_version(void);
 
 /*
@@ -159,6 +159,21 @@ typedef struct dt_attn_desc {
   int64_t tree_row_stride;       /* ... in k_tree and v_tree; 0 means Hkv*d */
   int64_t prefix_row_stride;     /* elements between consecutive cache rows of k_prefix/v_prefix */
   int64_t prefix_head_stride;    /* elements between consecutive KV heads within a cache row */
+  uint64_t* phase_stamps;        /* optional, for profiling (NULL: nothing is recorded): device
+                                    buffer, 8-byte aligned, of phase_stamp_rows rows of 8 uint64.
+                                    Row w belongs to the call's w-th workgroup, counting, launch
+                                    by launch, the forward kernel's workgroups and then the merge
+                                    kernel's (split rows only). Lane 0 of a workgroup writes the
+                                    GPU's 100 MHz real-time counter into its row's slots: forward
+                                    kernel 0 entry, 1 first K/V stage requested, 2 set-up done (Q in
+                                    registers, ancestor masks built), 3 first stage landed, 4 main
+                                    loop done, 5 outputs stored; merge kernel 0 entry, 5 outputs
+                                    stored; and slot 7 = 1 (forward) or 2 (merge) at entry. Other
+                                    slots, and those of phases a workgroup does not reach, are left
+                                    as they were; rows from phase_stamp_rows on are not written.
+                                    Recording uses separate kernel builds: with NULL the call runs
+                                    the same kernels as without this field. */
+  int64_t phase_stamp_rows;      /* rows of phase_stamps (>= 0) */
 } dt_attn_desc;
 
 /*

@@ -417,3 +417,69 @@ def test_fused_qkv_views_and_strided_output(n, P):
     assert torch.equal(out, ref_dev), "strided operands changed the result"
     assert bool((wide[:, :d] == 7.0).all()) and bool((wide[:, (Hq + 1) * d:] == 7.0).all()), "wrote outside the slice"
     assert_attention_close(host_f64(out), _oracle(ops, parents, [n], [P]), what=f"fused qkv n={n}")
+
+
+def test_phase_stamps():
+    """The optional phase stamps: the output is bit-identical with and without
+    them; every forward workgroup that stored outputs has non-decreasing stamps
+    for its phases (the first-stage stamp only where it visits keys) and every
+    merge block that stored outputs has entry <= stored; each row carries its
+    kernel's tag; a workgroup past the last work item stamps only its entry;
+    slot 6, rows past the call's workgroups and rows past the buffer are
+    untouched; over several launches (more sequences than one launch carries)
+    the rows keep counting."""
+    import torch
+
+    require_gpu()
+    Hq, Hkv, d = 8, 2, 128
+    parents, ops = _case([100], [3000], Hq, Hkv, d, ["recursive"], seed=57)
+    out, (q, kt, vt, kp, vp, par, layout) = _run(ops, parents, [100], [3000], Hq, Hkv, d)
+    buf = torch.full((4096, 8), -1, dtype=torch.int64, device="cuda")
+    print("phase stamps n=100 P=3000", flush=True)
+    out2 = dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, phase_stamps=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "phase stamps changed the output"
+    s = buf.cpu().numpy()
+    entered = s[:, 0] != -1
+    n_wg = int(entered.sum())
+    assert n_wg > 0 and entered[:n_wg].all() and not entered[n_wg:].any(), "rows past the call were written"
+    tag = s[:n_wg, 7]
+    assert set(np.unique(tag)) == {1, 2}, "a split call runs both kernels"
+    n_fwd = int((tag == 1).sum())
+    assert (tag[:n_fwd] == 1).all() and (tag[n_fwd:] == 2).all(), "forward rows first, then the merge's"
+    fwd, mrg = s[:n_fwd], s[n_fwd:n_wg]
+    stored = fwd[:, 5] != -1
+    assert stored.sum() > 0
+    ph = fwd[stored][:, :6]
+    always = ph[:, [0, 1, 2, 4, 5]]  # a work item with no keys to visit has no first stage (slot 3)
+    assert (always > 0).all() and (np.diff(always, axis=1) >= 0).all(), "phase stamps out of order"
+    landed = ph[:, 3] != -1
+    assert landed.any()
+    assert ((ph[landed, 3] >= ph[landed, 2]) & (ph[landed, 3] <= ph[landed, 4])).all()
+    assert (fwd[~stored][:, 1:7] == -1).all(), "a workgroup without a work item stamped past its entry"
+    mst = mrg[:, 5] != -1
+    assert mst.any() and (mrg[mst, 5] >= mrg[mst, 0]).all() and (mrg[:, 1:5] == -1).all()
+    assert mrg[mst, 0].min() >= ph[:, 5].max(), "the merge started before the forward kernel's last store"
+    assert (s[:, 6] == -1).all()
+    assert_attention_close(host_f64(out2), _oracle(ops, parents, [100], [3000]), what="phase stamps")
+
+    # several launches, a buffer shorter than the call's workgroups
+    rng = grng.stream(3, "many")
+    nodes = [int(x) for x in rng.integers(1, 40, size=70)]
+    plens = [int(x) for x in rng.integers(0, 130, size=70)]
+    parents, ops = _case(nodes, plens, 4, 1, 64, ["recursive", "deep"], seed=33)
+    out, (q, kt, vt, kp, vp, par, layout) = _run(ops, parents, nodes, plens, 4, 1, 64)
+    big = torch.full((4096, 8), -1, dtype=torch.int64, device="cuda")
+    dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, phase_stamps=big)
+    torch.cuda.synchronize()
+    e = (big[:, 0] != -1).cpu().numpy()
+    total = int(e.sum())
+    print(f"phase stamps over launches: {total} workgroups", flush=True)
+    assert e[:total].all() and bool(((big[:total, 7] == 1) | (big[:total, 7] == 2)).all())
+    rows = total - 5
+    big.fill_(-1)
+    out3 = dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, phase_stamps=big[:rows])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out3)
+    e = (big[:, 0] != -1).cpu().numpy()
+    assert e[:rows].all() and not e[rows:].any(), "rows past phase_stamp_rows were written"

@@ -43,7 +43,7 @@ def test_status_strings_and_version():
         s = dt.dt_status_string(code)
         assert s and s != "unknown status"
     assert dt.dt_status_string(-99) == "unknown status"
-    assert dt.dt_abi_version() >> 16 == 1
+    assert dt.dt_abi_version() >> 16 == 2
 
 
 @pytest.mark.parametrize("seed", range(8))
