@@ -792,12 +792,21 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_fwd(const AttnParams p)
   }
 
   if constexpr (WN > 1) {
-    // few rows per workgroup: every lane stores its own row's groups
+    // few rows per workgroup: every lane stores its own row, 16 bytes at a time.
+    // For each pair of four-value groups (j4, j4 + 1) the half-waves swap one
+    // group through v_permlane32_swap, so that lane (lr, 0) holds dims
+    // 32i + 8 j4 .. + 7 and lane (lr, 1) dims 32i + 8 (j4 + 1) .. + 7.
     uint16_t* orow = row_dst(my_row);
+    typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) *reinterpret_cast<uint2*>(orow + i * 32 + j4 * 8 + hh * 4) = pack(i, j4);
+      for (int j4 = 0; j4 < 4; j4 += 2) {
+        const uint2 a = pack(i, j4), b = pack(i, j4 + 1);
+        const auto sx = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+        *reinterpret_cast<u32x4s*>(orow + i * 32 + j4 * 8 + hh * 8) = u32x4s{sx[0], sy[0], sx[1], sy[1]};
+      }
   } else {
     // 256 rows per workgroup, all of them finishing together across the chip:
     // the wave's 32 rows leave through a wave-private LDS buffer (32 rows of
