@@ -140,6 +140,8 @@ def test_attention_validation_errors():
         "seqs": (dict(num_seqs=0), _lib.DT_ERR_SHAPE),
         "stride": (dict(prefix_row_stride=129), _lib.DT_ERR_SHAPE),
         "qstride": (dict(q_row_stride=100), _lib.DT_ERR_SHAPE),
+        "stamp rows": (dict(phase_stamp_rows=-1), _lib.DT_ERR_SHAPE),
+        "stamp alignment": (dict(phase_stamps=4, phase_stamp_rows=16), _lib.DT_ERR_SHAPE),
     }
     for name, (kw, code) in bad.items():
         d, keep = _desc(**kw)
