@@ -37,11 +37,15 @@
 //    parent[i] < i, tree keys beyond the workgroup's last node are skipped.
 //  * When there are too few (sequence, KV head, row tile) units to occupy the
 //    GPU, each unit's keys are split into chunks; partial (O, m, l) go to the
-//    workspace (O as fp16 after an exact power-of-two scaling per row) and a
-//    second kernel merges them with log-sum-exp weights.
+//    workspace (O as fp16 after an exact power-of-two scaling per row), each
+//    workgroup's rows as one contiguous block, and a second kernel merges them
+//    with log-sum-exp weights.
 //  * Work items are ordered so that the row tiles sharing one key chunk are
 //    dispatched to the same XCD (workgroups go round-robin over the 8 XCDs),
 //    which keeps that chunk's K/V in one L2.
+//  * Both kernels have a second instantiation for profiling that records the
+//    GPU's real-time counter at fixed points of every workgroup (the
+//    descriptor's phase stamps); the default instantiation has none of it.
 
 #include <hip/hip_runtime.h>
 
