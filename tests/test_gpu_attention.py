@@ -483,3 +483,25 @@ def test_phase_stamps():
     assert torch.equal(out, out3)
     e = (big[:, 0] != -1).cpu().numpy()
     assert e[:rows].all() and not e[rows:].any(), "rows past phase_stamp_rows were written"
+
+
+@pytest.mark.parametrize("n,P,Hq,Hkv,d", [(16, 2500, 8, 2, 128), (40, 900, 8, 2, 128), (200, 3000, 8, 2, 128),
+                                          (300, 1500, 4, 1, 64), (12, 4000, 2, 2, 64)])
+def test_phase_stamps_builds_match_plain_ones(n, P, Hq, Hkv, d):
+    """The stamping instantiations of both kernels compute the same bits as the
+    plain ones for every tile shape (64-, 128- and 256-row tiles, d = 64 and
+    128, split and unsplit), and every forward workgroup that stored outputs
+    stamped its entry before its store."""
+    import torch
+
+    require_gpu()
+    parents, ops = _case([n], [P], Hq, Hkv, d, ["recursive"], seed=71 + n)
+    out, (q, kt, vt, kp, vp, par, layout) = _run(ops, parents, [n], [P], Hq, Hkv, d)
+    buf = torch.zeros((4096, 8), dtype=torch.int64, device="cuda")
+    print(f"phase-stamp build n={n} P={P} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    out2 = dt.dt_tree_attention(q, kt, vt, kp, vp, par, layout, phase_stamps=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "the stamping build changed the output"
+    s = buf.cpu().numpy()
+    fwd = s[(s[:, 7] == 1) & (s[:, 5] != 0)]
+    assert len(fwd) > 0 and (fwd[:, 5] >= fwd[:, 0]).all()
