@@ -134,6 +134,21 @@ def test_forced_key_splits(split):
     assert_attention_close(host_f64(out), _oracle(ops, parents, [100], [1000]), what=f"split {split}")
 
 
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 6, 3)])
+def test_forced_splits_over_several_launches(d, Hq, Hkv):
+    """More sequences than one launch carries, every one split into key chunks of
+    its own count: each launch's partials (chunk, KV head, packed row) and merge
+    rows stay within their sequence's region."""
+    require_gpu()
+    rng = grng.stream(5, "many-split")
+    nodes = [int(x) for x in rng.integers(1, 60, size=40)]
+    plens = [int(x) for x in rng.integers(0, 700, size=40)]
+    parents, ops = _case(nodes, plens, Hq, Hkv, d, ["recursive", "deep", "bfs"], seed=44)
+    print(f"40 sequences, split_keys=128, d={d}", flush=True)
+    out, _ = _run(ops, parents, nodes, plens, Hq, Hkv, d, split_keys=128)
+    assert_attention_close(host_f64(out), _oracle(ops, parents, nodes, plens), what="many split")
+
+
 @pytest.mark.parametrize("v_scale", [1e-3, 3e3])
 def test_split_partials_keep_precision_at_any_magnitude(v_scale):
     """Split sequences merge per-chunk partials; the merge must be exact up to
