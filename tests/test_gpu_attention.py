@@ -520,3 +520,51 @@ def test_phase_stamps_builds_match_plain_ones(n, P, Hq, Hkv, d):
     s = buf.cpu().numpy()
     fwd = s[(s[:, 7] == 1) & (s[:, 5] != 0)]
     assert len(fwd) > 0 and (fwd[:, 5] >= fwd[:, 0]).all()
+
+
+def test_binding_rejects_mistyped_or_short_tensors():
+    """The binding checks what the C library cannot see (dtypes, devices,
+    extents, output shapes) and raises ValueError before anything is enqueued;
+    the caller's output buffers stay untouched."""
+    import torch
+
+    require_gpu()
+    Hq, Hkv, d, n, P = 4, 2, 64, 10, 100
+    parents, ops = _case([n], [P], Hq, Hkv, d, ["recursive"], seed=3)
+    q, kt, vt = dev_bf16(ops["q"]), dev_bf16(ops["k_tree"]), dev_bf16(ops["v_tree"])
+    kp, vp = dev_bf16(ops["k_prefix"]), dev_bf16(ops["v_prefix"])
+    par = dev_i32(parents[0])
+    layout = dt.AttnLayout([0, n], [P])
+    out = torch.full((n, Hq, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    bad = [
+        dict(q=q.half()),                                  # operand dtype
+        dict(k_prefix=kp.float()),
+        dict(parent=par.long()),                           # int64 parent
+        dict(parent=par[: n - 1]),                         # too short
+        dict(q=q.cpu()),                                   # host tensor
+        dict(out=torch.empty((n, Hq, d), dtype=torch.float16, device="cuda")),
+        dict(out=torch.empty((n - 1, Hq, d), dtype=torch.bfloat16, device="cuda")),
+        dict(phase_stamps=torch.zeros((8, 4), dtype=torch.int64, device="cuda")),
+        dict(phase_stamps=torch.zeros((8, 8), dtype=torch.int32, device="cuda")),
+    ]
+    for kw in bad:
+        args = dict(q=q, k_tree=kt, v_tree=vt, k_prefix=kp, v_prefix=vp, parent=par, out=out)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            dt.dt_tree_attention(args["q"], args["k_tree"], args["v_tree"], args["k_prefix"], args["v_prefix"],
+                                 args["parent"], layout, out=args["out"],
+                                 **({"phase_stamps": kw["phase_stamps"]} if "phase_stamps" in kw else {}))
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()), "a rejected call wrote its output"
+    # the walk: int32 inputs of at least N entries, outputs of the right type and size
+    offs = [0, n]
+    tok = dev_i32(np.arange(n))
+    am = dev_i32(np.zeros(n))
+    for kw in [dict(parent=par.long()), dict(token=tok[: n - 2]), dict(argmax_idx=am.float()),
+               dict(path=torch.empty(n - 1, dtype=torch.int32, device="cuda")),
+               dict(accept_len=torch.empty(1, dtype=torch.int64, device="cuda"))]:
+        args = dict(parent=par, token=tok, argmax_idx=am)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            dt.dt_accept_path(offs, args["parent"], args["token"], args["argmax_idx"], path=args.get("path"),
+                              accept_len=args.get("accept_len"))
